@@ -1,0 +1,493 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself:
+hand-worked fixtures (tests/golden), closed forms, library routines the oracle
+does not use, brute force on tiny inputs, and invariants the pages fix.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import moe_oracle as mo
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def read_golden(name):
+    d = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            k, *v = line.split()
+            d[k] = v
+    return d
+
+
+class Cfg:
+    """Minimal routing config for the oracle."""
+
+    def __init__(self, **kw):
+        self.k = 2
+        self.gate = "softmax"
+        self.renorm = True
+        self.route_scale = 1.0
+        self.n_rgroups = 1
+        self.topk_rgroups = 1
+        self.rgroup_topn = 0
+        self.__dict__.update(kw)
+
+
+# ---------------------------------------------------------------- own exp / sigmoid
+
+def _ulp_err(y32, ref64):
+    ref32 = ref64.astype(np.float32)
+    ulp = np.spacing(np.abs(ref32)).astype(np.float64)
+    return np.abs(y32.astype(np.float64) - ref64) / ulp
+
+
+def test_expf_against_libm_dense_sample(olib):
+    # every 61st fp32 bit pattern over [-87, 88]: ~35M values, compared with
+    # the C library's double exp, must be within 2 ulp of the fp32 result
+    lo = np.float32(-87.0).view(np.uint32)
+    hi = np.float32(88.0).view(np.uint32)
+    neg = np.arange(np.uint32(0x80000000), lo + np.uint32(1), 61, dtype=np.uint32)
+    pos = np.arange(np.uint32(0), hi + np.uint32(1), 61, dtype=np.uint32)
+    for bits in (neg, pos):
+        x = bits.view(np.float32)
+        y = np.empty_like(x)
+        olib.oracle_expf_array(x.size, x.ctypes.data, y.ctypes.data)
+        err = _ulp_err(y, np.exp(x.astype(np.float64)))
+        assert err.max() <= 2.0, (x[np.argmax(err)], err.max())
+
+
+def test_expf_special_values(olib):
+    assert olib.oracle_expf(0.0) == 1.0
+    assert olib.oracle_expf(-0.0) == 1.0
+    assert olib.oracle_expf(-87.5) == 0.0
+    assert math.isinf(olib.oracle_expf(88.5))
+    # e^1 and e^-1 to 1 ulp
+    for v in (1.0, -1.0, 10.0, -20.0):
+        y = np.float32(olib.oracle_expf(v))
+        assert _ulp_err(np.array([y]), np.array([math.exp(v)]))[0] <= 1.0
+
+
+def test_sigmoid_closed_forms(olib):
+    assert olib.oracle_sigmoidf(0.0) == 0.5
+    assert olib.oracle_sigmoidf(100.0) == 1.0
+    assert olib.oracle_sigmoidf(-100.0) == 0.0
+    x = np.linspace(-20, 20, 4001, dtype=np.float32)
+    y = np.array([olib.oracle_sigmoidf(float(v)) for v in x], np.float32)
+    ref = 1.0 / (1.0 + np.exp(-x.astype(np.float64)))
+    assert (_ulp_err(y, ref) <= 3.0).all()
+    # symmetry sigma(-x) = 1 - sigma(x) (within a few ulp of 1)
+    ym = np.array([olib.oracle_sigmoidf(float(-v)) for v in x], np.float64)
+    assert np.abs(ym + y - 1.0).max() < 3e-7
+
+
+# ---------------------------------------------------------------- logits
+
+def test_logits_one_hot_extracts_gate_column():
+    rng = np.random.default_rng(0)
+    H, E = 7, 5
+    Wg = rng.standard_normal((E, H))
+    x = np.eye(H)[[3, 0, 6]]
+    l = mo.logits(x, Wg)
+    # token t with x = e_h scores expert e by Wg[e, h]
+    np.testing.assert_array_equal(l, Wg[:, [3, 0, 6]].T)
+
+
+def test_logits_against_plain_loops_and_bias():
+    rng = np.random.default_rng(1)
+    T, H, E, V = 5, 9, 6, 11
+    x = rng.standard_normal((T, H)).astype(np.float32)
+    Wg = rng.standard_normal((E, H)).astype(np.float32)
+    tok = rng.integers(0, V, T)
+    pref = np.stack([rng.permutation(E)[:2] for _ in range(V)]).astype(np.int32)
+    l0 = mo.logits(x, Wg)
+    for t in range(T):
+        for e in range(E):
+            s = 0.0
+            for h in range(H):
+                s += float(x[t, h]) * float(Wg[e, h])
+            assert abs(l0[t, e] - s) <= 1e-12 * (1 + abs(s))
+    l1 = mo.logits(x, Wg, tok, pref, 3.0)
+    d = l1 - l0
+    for t in range(T):
+        for e in range(E):
+            assert abs(d[t, e] - (3.0 if e in pref[tok[t]] else 0.0)) < 1e-12
+
+
+def test_logits_bf16_decoding():
+    # bf16 bit patterns decode exactly: 0x3f80 = 1.0, 0xc000 = -2.0, 0x3e80 = 0.25
+    a = np.array([0x3F80, 0xC000, 0x3E80], np.uint16)
+    np.testing.assert_array_equal(mo.f64(a), [1.0, -2.0, 0.25])
+
+
+# ---------------------------------------------------------------- selection
+
+def test_select_golden():
+    g = read_golden("topk_worked_example.txt")
+    key = np.array([g["plain_key"]], np.float32)
+    sel = mo.select(key, int(g["plain_k"][0]))
+    assert sel[0].tolist() == [int(v) for v in g["plain_sel"]]
+    key = np.array([g["grouped_key"]], np.float32)
+    sel = mo.select(key, int(g["grouped_k"][0]), None, int(g["grouped_n_rgroups"][0]),
+                    int(g["grouped_topk_rgroups"][0]), int(g["grouped_rgroup_topn"][0]))
+    assert sel[0].tolist() == [int(v) for v in g["grouped_sel"]]
+    sel = mo.select(key, int(g["grouped_k"][0]))
+    assert sel[0].tolist() == [int(v) for v in g["grouped_plain_sel"]]
+
+
+def _brute_topk(row, k, allowed=None):
+    ids = [e for e in range(len(row)) if allowed is None or allowed[e]]
+    return sorted(ids, key=lambda e: (-float(row[e]), e))[:k]
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_select_brute_force_with_ties(seed):
+    rng = np.random.default_rng(seed)
+    T, E = 40, 8
+    # coarse values force many exact ties
+    key = (rng.integers(-3, 4, (T, E)) * 0.25).astype(np.float32)
+    for k in (1, 3, E):
+        sel = mo.select(key, k)
+        for t in range(T):
+            assert sel[t].tolist() == _brute_topk(key[t], k)
+    # k = 1 is numpy's argmax (first maximum)
+    np.testing.assert_array_equal(mo.select(key, 1)[:, 0], np.argmax(key, axis=1))
+    # k = E selects every expert
+    assert all(sorted(r) == list(range(E)) for r in mo.select(key, E).tolist())
+
+
+def test_select_signed_zero_is_a_tie():
+    key = np.array([[-0.0, 0.0, -1.0]], np.float32)
+    assert mo.select(key, 2)[0].tolist() == [0, 1]
+
+
+def test_select_ragged_k():
+    rng = np.random.default_rng(3)
+    key = rng.standard_normal((6, 10)).astype(np.float32)
+    k_tok = np.array([1, 4, 0, 4, 2, 3], np.int32)
+    sel = mo.select(key, 4, k_tok)
+    for t in range(6):
+        kt = k_tok[t]
+        assert sel[t, :kt].tolist() == _brute_topk(key[t], kt)
+        assert (sel[t, kt:] == -1).all()
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_select_grouped_properties(seed):
+    rng = np.random.default_rng(seed)
+    T, E, G, keep, topn, k = 30, 24, 6, 3, 2, 5
+    key = (rng.integers(-4, 5, (T, E)) * 0.125).astype(np.float32)
+    sel = mo.select(key, k, None, G, keep, topn)
+    gs = E // G
+    for t in range(T):
+        score = []
+        for g in range(G):
+            v = sorted(key[t, g * gs:(g + 1) * gs].tolist(), reverse=True)[:topn]
+            score.append(np.float32(np.float32(v[0]) + np.float32(v[1])))
+        kept = sorted(range(G), key=lambda g: (-score[g], g))[:keep]
+        allowed = [(e // gs) in kept for e in range(E)]
+        assert sel[t].tolist() == _brute_topk(key[t], k, allowed)
+        assert all((e // gs) in kept for e in sel[t])
+    # keeping every group, or a single group, reduces to plain top-k
+    np.testing.assert_array_equal(mo.select(key, k, None, G, G, topn), mo.select(key, k))
+    np.testing.assert_array_equal(mo.select(key, k, None, 1, 1, topn), mo.select(key, k))
+
+
+# ---------------------------------------------------------------- weights
+
+def test_softmax_weights_closed_forms():
+    # logits (ln 3, 0, 0, 0): softmax (1/2, 1/6, 1/6, 1/6)
+    l = np.array([[math.log(3.0), 0.0, 0.0, 0.0]])
+    sel, w = mo.route(l, Cfg(k=2, renorm=True))
+    assert sel[0].tolist() == [0, 1]
+    np.testing.assert_allclose(w[0], [0.75, 0.25], rtol=1e-12)
+    # without renormalisation the weights are the full-softmax probabilities
+    sel, w = mo.route(l, Cfg(k=2, renorm=False))
+    np.testing.assert_allclose(w[0], [0.5, 1.0 / 6.0], rtol=1e-12)
+
+
+def test_softmax_renorm_equals_softmax_of_selected():
+    rng = np.random.default_rng(5)
+    l = rng.standard_normal((20, 16)) * 3
+    sel, w = mo.route(l, Cfg(k=5, renorm=True))
+    for t in range(20):
+        ls = l[t, sel[t]]
+        ref = np.exp(ls - ls.max()) / np.exp(ls - ls.max()).sum()
+        np.testing.assert_allclose(w[t], ref, rtol=1e-12)
+    np.testing.assert_allclose(w.sum(axis=1), 1.0, rtol=1e-12)
+    assert (w > 0).all()
+
+
+def test_sigmoid_weights_sum_to_scale():
+    rng = np.random.default_rng(6)
+    l = rng.standard_normal((16, 32))
+    b = rng.uniform(-0.1, 0.1, 32).astype(np.float32)
+    cfg = Cfg(k=4, gate="sigmoid_grouped", route_scale=2.5, n_rgroups=4, topk_rgroups=2,
+              rgroup_topn=2)
+    sel, w = mo.route(l, cfg, ebias=b)
+    np.testing.assert_allclose(w.sum(axis=1), 2.5, rtol=1e-12)
+    assert (w > 0).all()
+    # zero logits: every sigmoid is 1/2, so equal weights 2.5/k
+    sel, w = mo.route(np.zeros((1, 32)), cfg)
+    np.testing.assert_allclose(w[0], 2.5 / 4)
+    # the bias steers selection only: weights use the unbiased sigmoid
+    l1 = np.zeros((1, 32)); l1[0, 5] = 1.0
+    sel, w = mo.route(l1, cfg, ebias=np.where(np.arange(32) == 9, 0.5, 0.0).astype(np.float32))
+    assert sel[0, 0] == 9 and sel[0, 1] == 5
+    s5 = 1 / (1 + math.exp(-1.0))
+    np.testing.assert_allclose(w[0, :2], 2.5 * np.array([0.5, s5]) / (0.5 * 3 + s5))
+
+
+# ---------------------------------------------------------------- expert FFN
+
+def test_ffn_closed_form_with_permutation_weights():
+    # W1 = diag(a) P1, W3 = P2, W2 = P3 with distinct permutations:
+    # y = P3 (silu(a * P1 x) * (P2 x)); a transposed operand gives another answer
+    rng = np.random.default_rng(7)
+    n = 6
+    P1, P2, P3 = (np.eye(n)[rng.permutation(n)] for _ in range(3))
+    a = rng.uniform(0.5, 2.0, n)
+    x = rng.standard_normal((4, n))
+    y = mo.ffn(x, np.diag(a) @ P1, P2, P3)
+    for t in range(4):
+        g = a * (P1 @ x[t])
+        u = P2 @ x[t]
+        ref = P3 @ (g / (1 + np.exp(-g)) * u)
+        np.testing.assert_allclose(y[t], ref, rtol=1e-13, atol=1e-15)
+
+
+def test_ffn_against_plain_loops():
+    rng = np.random.default_rng(8)
+    H, I = 5, 3
+    x = rng.standard_normal((2, H))
+    W1, W3 = rng.standard_normal((I, H)), rng.standard_normal((I, H))
+    W2 = rng.standard_normal((H, I))
+    y = mo.ffn(x, W1, W3, W2)
+    for t in range(2):
+        act = []
+        for i in range(I):
+            g = sum(W1[i, h] * x[t, h] for h in range(H))
+            u = sum(W3[i, h] * x[t, h] for h in range(H))
+            act.append(g / (1 + math.exp(-g)) * u)
+        for h in range(H):
+            assert abs(y[t, h] - sum(W2[h, i] * act[i] for i in range(I))) < 1e-12
+
+
+def test_silu_values():
+    assert mo.silu(np.array([0.0]))[0] == 0.0
+    np.testing.assert_allclose(mo.silu(np.array([1.0])), [1 / (1 + math.exp(-1))])
+    np.testing.assert_allclose(mo.silu(np.array([40.0])), [40.0])
+
+
+def test_sub_experts_sum_to_parent():
+    # MoE-Prism: sub-experts are neuron slices of a monolithic expert, so the
+    # slices' outputs add up to the parent's (MoE-Prism technical summary §2A)
+    from token_routing_shuffle_amd import workload as wl
+    cfg = wl.LayerConfig("t", 9, T=8, H=16, E=8, k=2, I=4, P=2, V=32, dtype="f32",
+                         gate="softmax", renorm=True, sub_split=4)
+    w = wl.make_weights(cfg)
+    W13, W2 = w["W13"].numpy(), w["W2"].numpy()
+    x = np.random.default_rng(0).standard_normal((3, 16))
+    parent_cfg = cfg.replace(E=2, I=16, sub_split=1)
+    # rebuild parent 1 from its slices: W1 rows and W3 rows stacked, W2 columns side by side
+    W1p = np.concatenate([W13[4 + s, :4] for s in range(4)])
+    W3p = np.concatenate([W13[4 + s, 4:] for s in range(4)])
+    W2p = np.concatenate([W2[4 + s] for s in range(4)], axis=1)
+    total = sum(mo.expert_ffn(x, W13, W2, 4 + s, 4) for s in range(4))
+    np.testing.assert_allclose(total, mo.ffn(x, W1p, W3p, W2p), rtol=1e-12, atol=1e-12)
+    del parent_cfg
+
+
+def test_shared_experts_sum_equals_concatenated():
+    rng = np.random.default_rng(9)
+    H, Is, ns = 6, 4, 2
+    W1 = [rng.standard_normal((Is, H)) for _ in range(ns)]
+    W3 = [rng.standard_normal((Is, H)) for _ in range(ns)]
+    W2 = [rng.standard_normal((H, Is)) for _ in range(ns)]
+    Wsh13 = np.concatenate(W1 + W3)
+    Wsh2 = np.concatenate(W2, axis=1)
+    x = rng.standard_normal((3, H))
+    y = mo.shared_ffn(x, Wsh13, Wsh2, ns, Is)
+    ref = sum(mo.ffn(x, W1[s], W3[s], W2[s]) for s in range(ns))
+    np.testing.assert_allclose(y, ref, rtol=1e-13)
+
+
+# ---------------------------------------------------------------- MoE output
+
+def test_moe_output_single_expert_is_dense_ffn():
+    rng = np.random.default_rng(10)
+    T, H, I = 5, 8, 4
+    W13 = rng.standard_normal((1, 2 * I, H))
+    W2 = rng.standard_normal((1, H, I))
+    x = rng.standard_normal((T, H))
+    sel = np.zeros((T, 1), np.int32)
+    out = mo.moe_output(x, sel, np.ones((T, 1)), W13, W2, I)
+    np.testing.assert_allclose(out, mo.ffn(x, W13[0, :I], W13[0, I:], W2[0]), rtol=1e-13)
+
+
+def test_moe_output_weighted_sum_and_relabelling():
+    rng = np.random.default_rng(11)
+    T, H, I, E, k = 6, 8, 4, 5, 2
+    W13 = rng.standard_normal((E, 2 * I, H))
+    W2 = rng.standard_normal((E, H, I))
+    x = rng.standard_normal((T, H))
+    sel = np.stack([rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    w = rng.uniform(0, 1, (T, k))
+    out = mo.moe_output(x, sel, w, W13, W2, I)
+    for t in range(T):
+        ref = sum(w[t, j] * mo.ffn(x[t:t + 1], W13[sel[t, j], :I], W13[sel[t, j], I:],
+                                   W2[sel[t, j]])[0] for j in range(k))
+        np.testing.assert_allclose(out[t], ref, rtol=1e-12)
+    # relabel experts (weights and selections together): output unchanged
+    pi = rng.permutation(E)
+    inv = np.argsort(pi)
+    out2 = mo.moe_output(x, pi[sel].astype(np.int32), w, W13[inv], W2[inv], I)
+    np.testing.assert_array_equal(out, out2)
+
+
+# ---------------------------------------------------------------- shuffle
+
+def _golden_shuffle():
+    g = read_golden("shuffle_worked_example.txt")
+    iv = lambda k: np.array([int(v) for v in g[k]], np.int32)  # noqa: E731
+    return g, iv
+
+
+def test_shuffle_golden():
+    g, iv = _golden_shuffle()
+    E, P = int(g["E"][0]), int(g["P"][0])
+    r = mo.shuffle(iv("row_ptr"), iv("topk_slot"), iv("tok"), iv("lut"), E, P)
+    for key in ("g_pred", "sorted_to_assign", "assign_to_sorted", "expert_count",
+                "expert_off", "group_count", "group_off", "tok_perm", "tok_off"):
+        np.testing.assert_array_equal(r[key], iv(key), err_msg=key)
+    np.testing.assert_array_equal(r["pair_count"].reshape(-1), iv("pair_count"))
+    assert r["lar"] == float(g["lar"][0])
+
+
+def _brute_shuffle(row_ptr, slot, tok, lut, E, P):
+    T = len(row_ptr) - 1
+    items = []
+    for t in range(T):
+        for a in range(row_ptr[t], row_ptr[t + 1]):
+            items.append(((int(slot[a]), int(lut[tok[t]]), t), a))
+    items.sort()
+    s2a = [a for _, a in items]
+    toks = sorted(range(T), key=lambda t: (int(lut[tok[t]]), t))
+    return s2a, toks
+
+
+def _random_routing(rng, T, E, k_max, ragged):
+    k_tok = rng.integers(0, k_max + 1, T) if ragged else np.full(T, k_max)
+    row_ptr = mo.row_ptr_of(k_tok)
+    slot = np.concatenate([rng.permutation(E)[:k] for k in k_tok]).astype(np.int32) \
+        if row_ptr[-1] else np.zeros(0, np.int32)
+    return row_ptr, slot
+
+
+@pytest.mark.parametrize("seed,T,E,P,k,ragged", [
+    (0, 13, 8, 2, 3, False), (1, 20, 8, 4, 2, True), (2, 1, 4, 1, 4, False),
+    (3, 9, 6, 6, 1, False), (4, 17, 16, 4, 5, True), (5, 0, 4, 2, 2, False),
+])
+def test_shuffle_brute_force_and_invariants(seed, T, E, P, k, ragged):
+    rng = np.random.default_rng(seed)
+    V = 11
+    row_ptr, slot = _random_routing(rng, T, E, k, ragged)
+    tok = rng.integers(0, V, T).astype(np.int32)
+    lut = rng.integers(0, P, V).astype(np.int32)
+    r = mo.shuffle(row_ptr, slot, tok, lut, E, P)
+    s2a, toks = _brute_shuffle(row_ptr, slot, tok, lut, E, P)
+    assert r["sorted_to_assign"].tolist() == s2a
+    assert r["tok_perm"].tolist() == toks
+    A = int(row_ptr[-1])
+    # bijections
+    assert sorted(r["sorted_to_assign"].tolist()) == list(range(A))
+    assert (r["assign_to_sorted"][r["sorted_to_assign"]] == np.arange(A)).all()
+    assert sorted(r["tok_perm"].tolist()) == list(range(T))
+    # counts sum to the number of assignments
+    assert r["expert_count"].sum() == r["group_count"].sum() == r["pair_count"].sum() == A
+    np.testing.assert_array_equal(r["expert_count"], np.bincount(slot, minlength=E))
+    np.testing.assert_array_equal(r["expert_off"], np.concatenate([[0], np.cumsum(r["expert_count"])]))
+    # every row sits inside its expert's range, which sits inside its group's range
+    epg = E // P
+    t_of_a = np.repeat(np.arange(T), np.diff(row_ptr))
+    for a in range(A):
+        s = r["assign_to_sorted"][a]
+        e = slot[a]
+        g = e // epg
+        assert r["expert_off"][e] <= s < r["expert_off"][e + 1]
+        assert r["group_off"][g] <= s < r["group_off"][g + 1]
+        assert r["g_pred"][t_of_a[a]] == lut[tok[t_of_a[a]]]
+    # every token lands in the segment of its predicted group
+    for i, t in enumerate(r["tok_perm"]):
+        gp = lut[tok[t]]
+        assert r["tok_off"][gp] <= i < r["tok_off"][gp + 1]
+    # pair_count is the predicted-group x expert-group histogram
+    pc = np.zeros((P, P), int)
+    for a in range(A):
+        pc[lut[tok[t_of_a[a]]], slot[a] // epg] += 1
+    np.testing.assert_array_equal(r["pair_count"], pc)
+    if A:
+        assert r["lar"] == np.trace(pc) / A
+
+
+def test_shuffle_single_group_is_stable_sort_by_expert():
+    rng = np.random.default_rng(12)
+    row_ptr, slot = _random_routing(rng, 30, 8, 3, False)
+    tok = rng.integers(0, 50, 30).astype(np.int32)
+    r = mo.shuffle(row_ptr, slot, tok, np.zeros(50, np.int32), 8, 1)
+    np.testing.assert_array_equal(r["sorted_to_assign"], np.argsort(slot, kind="stable"))
+    assert r["lar"] == 1.0
+
+
+def test_gather_and_combine_restore_order():
+    rng = np.random.default_rng(13)
+    T, E, P, k, H = 12, 8, 4, 3, 5
+    row_ptr, slot = _random_routing(rng, T, E, k, False)
+    tok = rng.integers(0, 20, T)
+    lut = rng.integers(0, P, 20)
+    r = mo.shuffle(row_ptr, slot, tok, lut, E, P)
+    x = rng.standard_normal((T, H))
+    xs = mo.gather(x, r["sorted_to_assign"], row_ptr)
+    t_of_a = np.repeat(np.arange(T), k)
+    for s in range(T * k):
+        np.testing.assert_array_equal(xs[s], x[t_of_a[r["sorted_to_assign"][s]]])
+    # weights summing to 1 per token and y_sorted = x_sorted: combine returns x
+    w = rng.uniform(0.1, 1, (T, k))
+    w /= w.sum(axis=1, keepdims=True)
+    out = mo.combine(xs, r["assign_to_sorted"], row_ptr, w.reshape(-1))
+    np.testing.assert_allclose(out, x, rtol=1e-14, atol=1e-15)
+    # k = 1 with weight 1: combine is exactly the inverse permutation
+    row_ptr1, slot1 = _random_routing(rng, T, E, 1, False)
+    r1 = mo.shuffle(row_ptr1, slot1, tok, lut, E, P)
+    xs1 = mo.gather(x, r1["sorted_to_assign"], row_ptr1)
+    np.testing.assert_array_equal(mo.combine(xs1, r1["assign_to_sorted"], row_ptr1, np.ones(T)), x)
+    # shared output is added once
+    ysh = rng.standard_normal((T, H))
+    np.testing.assert_allclose(
+        mo.combine(xs, r["assign_to_sorted"], row_ptr, w.reshape(-1), ysh), x + ysh, rtol=1e-13)
+
+
+def test_build_lut_hand_example():
+    # 3 token IDs, E=4 original experts placed as slots perm=[2,0,3,1], P=2
+    perm = np.array([2, 0, 3, 1])           # expert 0 -> slot 2 (group 1), ...
+    prof_tok = np.array([0, 0, 1, 2])
+    sel = np.array([[0, 2], [2, 1], [1, 3], [-1, -1]])   # token 2 routed nowhere
+    # token 0: experts 0,2 -> groups 1,1 ; experts 2,1 -> groups 1,0 => 3x g1, 1x g0
+    # token 1: experts 1,3 -> groups 0,0 ; tokens 2, 3 unseen -> v mod 2
+    lut = mo.build_lut(prof_tok, sel, perm, 4, 2, 4)
+    assert lut.tolist() == [1, 0, 0, 1]
+    # a tie goes to the lower group
+    lut = mo.build_lut(np.array([0]), np.array([[0, 1]]), perm, 4, 2, 1)
+    assert lut.tolist() == [0]
+
+
+def test_relative_error_metric():
+    ref = np.array([[1.0, -4.0], [0.5, 0.25]])
+    y = ref + np.array([[0.04, 0.0], [0.0, 0.01]])
+    assert mo.relative_error(y, ref) == pytest.approx(0.02)
