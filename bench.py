@@ -1,0 +1,211 @@
+#!/usr/bin/env python3
+"""Benchmark: one MoE layer forward (route -> shuffle -> expert FFN -> combine)
+on one MI355X, DeepSeek-V2-Lite-shaped layer (T=4096 tokens, H=2048, 64 routed
+experts top-6 + 2 shared, I=1408, P=8 placement groups), seeded synthetic
+inputs resident in HBM.
+
+Prints one JSON line: tokens/s over the timed steps, the roofline position of
+the dominant kernel (the grouped GEMM1 + SwiGLU launch, timed with HIP events
+recorded around it on the layer's stream) and the CPU oracle timed on a
+bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+WORKLOAD = "dsv2lite"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--fuse-gather", type=int, default=int(os.environ.get("MOE_BENCH_FUSE_GATHER", "1")))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=256, help="tokens in the oracle's timed sample")
+    return ap.parse_args()
+
+
+def algorithmic(cfg, A):
+    """Algorithmic work per launch of each stage (bytes or flops)."""
+    T, H, I, E = cfg.T, cfg.H, cfg.I, cfg.E
+    b = 2 if cfg.dtype == "bf16" else 4
+    Ish = cfg.n_shared * cfg.I_shared
+    return {
+        # flops of the grouped GEMM1 (+SwiGLU): routed rows and shared experts
+        "ffn_up_flops": 2.0 * A * H * 2 * I + 2.0 * T * H * 2 * Ish,
+        "ffn_down_flops": 2.0 * A * I * H + 2.0 * T * Ish * H,
+        # bytes: read x once, write A rows (+ 8T + 12A index metadata)
+        "dispatch_bytes": T * H * b + A * H * b + 8.0 * T + 12.0 * A,
+        # bytes: read A rows + weights/indices, write T rows (+ shared rows)
+        "combine_bytes": A * H * b + 8.0 * A + T * H * b + (T * H * b if Ish else 0),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the sharding design is described in DESIGN.md); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from token_routing_shuffle_amd import moe, offline
+    from token_routing_shuffle_amd import workload as wl
+
+    dev = "cuda"
+    cfg = wl.CONFIGS[args.workload]
+    tables = wl.make_tables(cfg)
+    w = wl.make_weights(cfg, dev)
+    x = wl.make_x(cfg, dev)
+    # offline: placement (slot-ordered weights) and token->group LUT from a
+    # 65536-token profiling draw routed by the library itself
+    d = offline.device_layer(cfg, tables, w, np.zeros(cfg.V, np.int32), dev)
+    prof_x = wl.make_prof_x(cfg, dev)
+    lut = offline.profile_lut(cfg, d, prof_x, tables.prof_tok)
+    d["lut"] = torch.as_tensor(lut, device=dev)
+    del prof_x
+    c = moe.make_cfg(cfg, fuse_gather=args.fuse_gather)
+    ws = moe.workspace(c)
+    T, E, P = cfg.T, cfg.E, cfg.P
+    tok = torch.as_tensor(tables.tok, device=dev)
+    k_tok = None if tables.k_tok is None else torch.as_tensor(tables.k_tok, device=dev)
+    out = torch.empty((T, cfg.H), dtype=torch.bfloat16 if cfg.dtype == "bf16" else torch.float32,
+                      device=dev)
+    row_ptr = torch.empty(T + 1, dtype=torch.int32, device=dev)
+    pair = torch.empty(P * P, dtype=torch.int32, device=dev)
+    ecount = torch.empty(E, dtype=torch.int32, device=dev)
+    W = moe.weights_struct(d)
+    X = moe.inputs_struct(x, tok, k_tok)
+    stream = torch.cuda.current_stream()
+
+    def make_events():
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * moe.MOE_NSTAGES)]
+        for e in evs:
+            e.record(stream)
+        return evs
+
+    base_ex = dict(row_ptr=row_ptr, pair_count=pair, expert_count=ecount)
+    for _ in range(args.warmup):
+        moe.moe_forward(c, W, X, out, moe.exports_struct(base_ex), ws)
+    torch.cuda.synchronize()
+    ev_sets = [make_events() for _ in range(args.steps)]
+    exs = [moe.exports_struct(base_ex, events=ev_sets[i]) for i in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        moe.moe_forward(c, W, X, out, exs[i], ws)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    stage_ms = {}
+    for si, name in enumerate(moe.STAGES):
+        v = [ev_sets[i][2 * si].elapsed_time(ev_sets[i][2 * si + 1]) for i in range(args.steps)]
+        stage_ms[name] = float(np.mean(v))
+
+    A = int(row_ptr[T].item())
+    pc = pair.cpu().numpy().reshape(P, P)
+    counts = ecount.cpu().numpy()
+    alg = algorithmic(cfg, A)
+    up_ms = stage_ms["ffn_up"]
+    achieved = alg["ffn_up_flops"] / (up_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
+                "traffic": None, "kernel": "k_grouped_gemm (GEMM1 + SwiGLU, routed + shared)",
+                "flops_per_launch": alg["ffn_up_flops"], "avg_launch_ms": round(up_ms, 4)}
+    secondary = {
+        "ffn_down_tflops": round(alg["ffn_down_flops"] / (stage_ms["ffn_down"] * 1e-3) / 1e12, 2),
+        "combine_gbs": round(alg["combine_bytes"] / (stage_ms["combine"] * 1e-3) / 1e9, 1),
+        "dispatch_gbs": round(alg["dispatch_bytes"] / ((stage_ms["shuffle"] + stage_ms["gather"] +
+                                                        stage_ms["ffn_up"] * 0) * 1e-3) / 1e9, 1)
+        if args.fuse_gather == 0 else None,
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, tables, w, x, np, torch, args.cpu_sample)
+
+    res = {
+        "metric": "MoE-layer tokens/s on 1 MI355X",
+        "value": round(T * 1e3 / ms_per_step, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic (seeded; Zipf token IDs, N(0,1) activations, N(0,1/fan_in) weights)",
+        "config": {"workload": "DeepSeek-V2-Lite-shaped MoE layer: T=%d H=%d E=%d top-%d softmax "
+                               "+%d shared, I=%d, P=%d, V=%d" % (T, cfg.H, E, cfg.k, cfg.n_shared,
+                                                                 cfg.I, P, cfg.V)
+                   if args.workload == "dsv2lite" else args.workload,
+                   "tokens": T, "assignments": A, "fuse_gather": args.fuse_gather,
+                   "lar": round(float(np.trace(pc)) / max(A, 1), 4),
+                   "max_over_mean_expert_load": round(float(counts.max() / max(counts.mean(), 1e-9)), 3)},
+        "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
+        "secondary": secondary,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(cfg, tables, w, x, np, torch, n_sample):
+    """The oracle (unchanged) on a bounded sample of the same layer: gate
+    logits, routing, dispatch metadata and the dense per-token MoE for the
+    first n_sample tokens; tokens/s = n_sample / wall time."""
+    from oracle import moe_oracle as mo
+
+    def h(t):
+        if t is None:
+            return None
+        t = t.detach()
+        if t.dtype == torch.bfloat16:
+            return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        return t.cpu().numpy()
+
+    hw = {k: h(v) for k, v in w.items()}
+    xs = h(x)[:n_sample]
+    tok = tables.tok[:n_sample]
+    k_tok = None if tables.k_tok is None else tables.k_tok[:n_sample]
+    t0 = time.perf_counter()
+    l64 = mo.logits(xs, hw["Wg"], tok, tables.pref, cfg.aff_bias if tables.pref is not None else 0.0)
+    sel, wt = mo.route(l64, cfg, k_tok, tables.ebias)
+    kt = k_tok if k_tok is not None else np.full(n_sample, cfg.k)
+    rp = mo.row_ptr_of(kt)
+    slot = tables.perm[sel[sel >= 0]]
+    lut = np.arange(cfg.V, dtype=np.int32) % cfg.P
+    mo.shuffle(rp, slot, tok, lut, cfg.E, cfg.P)
+    mo.moe_output(xs, sel, wt, hw["W13"], hw["W2"], cfg.I, hw.get("Wsh13"), hw.get("Wsh2"),
+                  cfg.n_shared, cfg.I_shared)
+    dt = time.perf_counter() - t0
+    threads = 1
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([1] + [i.get("num_threads", 1) for i in threadpool_info()])
+    except Exception:
+        pass
+    return {"value": round(n_sample / dt, 2), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle", "wall_s": round(dt, 2),
+            "sample": "first %d of %d tokens of the same layer (fp64 numpy oracle: logits, "
+                      "routing, dispatch metadata, dense per-token MoE incl. shared experts)"
+                      % (n_sample, cfg.T)}
+
+
+if __name__ == "__main__":
+    main()

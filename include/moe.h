@@ -1,0 +1,275 @@
+/*
+ * moe.h — C ABI of libmoe: one Mixture-of-Experts layer forward pass with
+ * affinity-aware token dispatch, on one AMD Instinct MI355X (gfx950).
+ *
+ * The method (Sem-MoE "semantic parallelism"; pages: "Semantic Parallelism:
+ * Redefining Efficient MoE Inference via Model-Data Co-Scheduling", Korean,
+ * German and Japanese summaries, and "MoE-Prism: Disentangling Monolithic
+ * Experts for Elastic MoE Services via Model-System Co-Designs"):
+ *   - each token activates only a few experts picked by the gate, and under
+ *     expert parallelism its row has to travel to the device holding them
+ *     (ko/de technical summary §1, ja technical overview §1);
+ *   - experts are placed on devices by shuffling the gate matrix's columns,
+ *     which moves experts physically without changing what the model computes
+ *     (ja technical overview §2.2A) — here: every per-expert tensor is stored
+ *     in "slot" order, slot = placement position, and the P placement groups
+ *     are the E/P consecutive slots [g*E/P, (g+1)*E/P);
+ *   - a lightweight table maps a token ID to the expert group it is predicted
+ *     to need (ja technical overview §2.3);
+ *   - before the MoE layer tokens are shuffled to the device of their predicted
+ *     experts, and after the experts the results are gathered back into the
+ *     original token order (de technical summary §2B, ja technical overview
+ *     §2.2B);
+ *   - MoE-Prism's sub-experts are neuron slices of a monolithic expert and the
+ *     routing budget k is a per-request knob (MoE-Prism technical summary §2A,
+ *     §1, §5) — here: ragged per-token k in CSR form.
+ * On one GPU there is no communication: the shuffle is a stable counting sort
+ * by (slot, predicted group, token) and the would-be all-to-all traffic is the
+ * P x P matrix pair_count.
+ *
+ * Conventions for every call
+ *   - All pointers are DEVICE pointers unless marked "host".  Row-major
+ *     layouts; per-expert tensors in slot order.  dtype MOE_BF16: activations
+ *     and weights are bf16 (uint16 bit patterns), accumulation fp32;
+ *     dtype MOE_F32: everything fp32.
+ *   - The caller owns every buffer.  The library allocates no device memory,
+ *     keeps no mutable global state and is re-entrant when concurrent calls
+ *     use distinct workspaces.  moe_workspace_bytes(cfg) bytes of workspace
+ *     (256-byte aligned) are enough for every call.
+ *   - Calls enqueue kernels on `stream` (a hipStream_t; NULL = the null
+ *     stream) and return without synchronising.  Device-side sizes that the
+ *     host cannot know (the number of assignments A = row_ptr[T] when k is
+ *     ragged) stay on the device; buffers sized by A are allocated for
+ *     A_max = T * k_max.
+ *   - Return value: MOE_OK (0) or a negative moe_status.  Argument checks
+ *     happen before anything is enqueued; MOE_EHIP reports a launch error
+ *     (hipGetLastError) and moe_last_error() gives its text.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum moe_status {
+    MOE_OK = 0,
+    MOE_EINVAL = -1,     /* null pointer or invalid argument value */
+    MOE_ESHAPE = -2,     /* unsupported or inconsistent sizes */
+    MOE_EDTYPE = -3,     /* unsupported dtype / gate combination */
+    MOE_EWORKSPACE = -4, /* workspace missing, too small or misaligned */
+    MOE_EHIP = -5        /* HIP runtime / launch error, see moe_last_error() */
+};
+
+enum moe_dtype { MOE_F32 = 0, MOE_BF16 = 1 };
+
+enum moe_gate {
+    MOE_GATE_SOFTMAX = 0,         /* softmax over all E logits */
+    MOE_GATE_SIGMOID_GROUPED = 1  /* sigmoid + per-expert bias, group-limited */
+};
+
+enum moe_ffn_which { MOE_FFN_ROUTED = 0, MOE_FFN_SHARED = 1 };
+
+/* Stages timed by moe_forward when moe_exports.events is set. */
+enum moe_stage {
+    MOE_STAGE_ROUTE = 0,    /* gate GEMM + top-k + weights */
+    MOE_STAGE_SHUFFLE = 1,  /* LUT lookup + counting sort metadata */
+    MOE_STAGE_GATHER = 2,   /* x -> x_sorted (skipped when fuse_gather) */
+    MOE_STAGE_FFN_UP = 3,   /* grouped GEMM1 + SwiGLU, routed and shared */
+    MOE_STAGE_FFN_DOWN = 4, /* grouped GEMM2, routed and shared */
+    MOE_STAGE_COMBINE = 5,  /* weighted combine back to token order */
+    MOE_NSTAGES = 6
+};
+
+/* Layer description (host struct). */
+typedef struct moe_cfg {
+    int32_t T;            /* tokens */
+    int32_t H;            /* hidden size */
+    int32_t E;            /* routed experts (or sub-experts) */
+    int32_t P;            /* placement groups; E % P == 0, E/P a power of 2 */
+    int32_t I;            /* routed expert intermediate size */
+    int32_t k_max;        /* top-k; with ragged, the largest per-token k */
+    int32_t ragged;       /* 1: per-token k from k_tok[] */
+    int32_t n_shared;     /* always-on shared experts (weight 1) */
+    int32_t I_shared;     /* intermediate size of each shared expert */
+    int32_t V;            /* vocabulary size (token IDs in [0, V)) */
+    int32_t n_pref;       /* preferred experts per token ID (affinity table width) */
+    int32_t dtype;        /* moe_dtype */
+    int32_t gate;         /* moe_gate */
+    int32_t renorm;       /* softmax: 1 = renormalise weights over the selected */
+    float route_scale;    /* sigmoid gate: weights scaled to sum to route_scale */
+    int32_t n_rgroups;    /* sigmoid gate: routing groups (contiguous original ids) */
+    int32_t topk_rgroups; /* sigmoid gate: routing groups kept */
+    int32_t rgroup_topn;  /* sigmoid gate: a group's score sums its top-n keys */
+    float aff_bias;       /* logit bias on a token's preferred experts */
+    int32_t fuse_gather;  /* moe_forward: 1 = GEMM1 reads x rows through the
+                             permutation instead of materialising x_sorted */
+} moe_cfg;
+
+/*
+ * Host only; needs no GPU.  Checks the description: positive T, H, E, P, I,
+ * V; k_max in [1, min(E, 64)]; E % P == 0 and E/P a power of two; E*P <= 4096;
+ * E <= 512; n_pref in [0, E]; for bf16 H % 128 == 0, I % 64 == 0 and
+ * (n_shared*I_shared) % 64 == 0; sigmoid gate only with n_rgroups dividing E,
+ * 1 <= topk_rgroups <= n_rgroups, 1 <= rgroup_topn <= E/n_rgroups, and at
+ * least k_max experts in the kept groups.  Returns MOE_OK or the error code.
+ */
+int32_t moe_validate(const moe_cfg* cfg);
+
+/* Host only.  Workspace bytes enough for every call with this cfg (0 if the
+ * cfg is invalid). */
+size_t moe_workspace_bytes(const moe_cfg* cfg);
+
+/* Text of the last error on the calling thread (never NULL). */
+const char* moe_last_error(void);
+
+/*
+ * Route: gate GEMM (MFMA), affinity bias, top-k selection and weights.
+ *   x[T,H]          activations
+ *   Wg[E,H]         gate rows in slot order (the shuffled gate columns)
+ *   ebias[E]        fp32 per-expert selection bias in slot order, or NULL
+ *                   (sigmoid gate only; enters selection, not the weights)
+ *   slot_to_orig[E] original expert id of each slot (tie-break and routing
+ *                   groups use original ids)
+ *   tok[T]          token IDs in [0, V)
+ *   pref[V,n_pref]  preferred ORIGINAL expert ids per token ID, or NULL; the
+ *                   gate adds aff_bias to those logits (synthetic affinity)
+ *   k_tok[T]        per-token k in [0, k_max] when ragged, else ignored
+ * Outputs:
+ *   row_ptr[T+1]    CSR offsets, exclusive scan of k_t (A = row_ptr[T])
+ *   topk_slot[A_max] selected slots, token-major, in selection order:
+ *                   key descending, ties to the lower ORIGINAL id.  Keys:
+ *                   softmax gate — the fp32 logit; sigmoid gate —
+ *                   sigmoid(l) + ebias, with sigmoid on an exp evaluated as
+ *                   Cody-Waite reduction + degree-7 Taylor polynomial in fp32
+ *                   fused multiply-adds (bit-reproducible).
+ *   topk_w[A_max]   fp32 weights: softmax p_j (renorm: p_j / sum of selected
+ *                   p); sigmoid: route_scale * s_j / sum_j s_j, s = sigmoid(l)
+ *   logits[T,E]     optional fp32 export of the biased logits, slot order
+ * Workspace: unused (may be NULL).
+ */
+int32_t moe_route(const moe_cfg* cfg, const void* x, const void* Wg, const float* ebias,
+                  const int32_t* slot_to_orig, const int32_t* tok, const int32_t* pref,
+                  const int32_t* k_tok, int32_t* row_ptr, int32_t* topk_slot, float* topk_w,
+                  float* logits, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Shuffle: token->group lookup and the dispatch metadata (Sem-MoE's token
+ * shuffle by predicted device, done on one GPU as a stable counting sort).
+ *   row_ptr, topk_slot  as produced by moe_route
+ *   tok[T], lut[V]      lut[v] in [0, P): predicted placement group of token ID v
+ *   x[T,H]              activations (read only if x_sorted != NULL)
+ * Outputs (int32):
+ *   expert_count[E], expert_off[E+1]   rows per slot and their offsets
+ *   group_count[P], group_off[P+1]     rows per placement group
+ *   pair_count[P*P]     [p*P + g] = assignments of tokens predicted for group
+ *                       p whose expert is in group g (the all-to-all matrix;
+ *                       trace / A is the local activation rate)
+ *   tok_perm[T], tok_off[P+1]  tokens ordered by (predicted group, token)
+ *   sorted_to_assign[A_max]    assignment index of each sorted row; rows are
+ *                       ordered by (slot, predicted group, token), so each
+ *                       slot's rows are contiguous and each group's slots are
+ *   assign_to_sorted[A_max]    inverse permutation
+ *   x_sorted[A_max,H]   optional: x_sorted[s] = x[token of row s]; NULL skips
+ * Workspace: required.
+ */
+int32_t moe_shuffle(const moe_cfg* cfg, const int32_t* row_ptr, const int32_t* topk_slot,
+                    const int32_t* tok, const int32_t* lut, const void* x,
+                    int32_t* expert_count, int32_t* expert_off, int32_t* group_count,
+                    int32_t* group_off, int32_t* pair_count, int32_t* tok_perm, int32_t* tok_off,
+                    int32_t* sorted_to_assign, int32_t* assign_to_sorted, void* x_sorted,
+                    void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Expert FFN (grouped SwiGLU GEMMs on MFMA): for each row r of an expert e,
+ *   y[r] = W2_e (silu(W1_e x_r) * (W3_e x_r)), fp32 accumulation; with bf16
+ *   the intermediate is rounded to bf16 before the down projection.
+ * which == MOE_FFN_ROUTED:
+ *   rows [expert_off[e], expert_off[e+1]) of slots e in [e_begin, e_end)
+ *   (one placement group's range is one device's share);
+ *   x_sorted[A_max,H] holds the rows, or is NULL: then row s is read from
+ *   x[t] with t the token of assignment sorted_to_assign[s] (CSR row_ptr);
+ *   W13[E,2I,H]: rows [0,I) = W1_e, rows [I,2I) = W3_e;  W2[E,H,I];
+ *   y[A_max,H]: rows written at their sorted positions.
+ * which == MOE_FFN_SHARED: all T rows of x[T,H] through the n_shared shared
+ *   experts stacked along the intermediate axis (their sum):
+ *   W13 = Wsh13[2*ns*Is, H] (all W1 rows, then all W3 rows), W2 = Wsh2[H, ns*Is];
+ *   y[T,H].  x_sorted, sorted_to_assign, row_ptr, expert_off, e_begin, e_end
+ *   are ignored.
+ * Workspace: required.
+ */
+int32_t moe_expert_ffn(const moe_cfg* cfg, int32_t which, const void* x_sorted, const void* x,
+                       const int32_t* row_ptr, const int32_t* sorted_to_assign,
+                       const int32_t* expert_off, const void* W13, const void* W2,
+                       int32_t e_begin, int32_t e_end, void* y, void* ws, size_t ws_bytes,
+                       void* stream);
+
+/*
+ * Combine (restore token order): out[t] = sum_{j<k_t} topk_w[a] *
+ * y_sorted[assign_to_sorted[a]] + y_sh[t], a = row_ptr[t] + j, summed in fp32
+ * in j order then rounded to the dtype.  Deterministic, no atomics.
+ *   y_sh[T,H] shared-expert output or NULL.
+ */
+int32_t moe_combine(const moe_cfg* cfg, const void* y_sorted, const int32_t* assign_to_sorted,
+                    const int32_t* row_ptr, const float* topk_w, const void* y_sh, void* out,
+                    void* stream);
+
+/* Device tensors of one layer for moe_forward (host struct of device pointers). */
+typedef struct moe_weights {
+    const void* Wg;              /* [E,H] slot order */
+    const float* ebias;          /* [E] slot order, or NULL */
+    const int32_t* slot_to_orig; /* [E] */
+    const void* W13;             /* [E,2I,H] slot order */
+    const void* W2;              /* [E,H,I] slot order */
+    const void* Wsh13;           /* [2*ns*Is,H] or NULL when n_shared == 0 */
+    const void* Wsh2;            /* [H,ns*Is] or NULL */
+    const int32_t* lut;          /* [V] */
+    const int32_t* pref;         /* [V,n_pref] original ids, or NULL */
+} moe_weights;
+
+typedef struct moe_inputs {
+    const void* x;        /* [T,H] */
+    const int32_t* tok;   /* [T] */
+    const int32_t* k_tok; /* [T] when ragged, else NULL */
+} moe_inputs;
+
+/* Optional outputs of moe_forward; every NULL member is kept in the
+ * workspace instead.  events: 2*MOE_NSTAGES hipEvent_t handles (or NULL);
+ * events[2*s] and events[2*s+1] are recorded on the stream before and after
+ * stage s. */
+typedef struct moe_exports {
+    float* logits;
+    int32_t* row_ptr;
+    int32_t* topk_slot;
+    float* topk_w;
+    int32_t* expert_count;
+    int32_t* expert_off;
+    int32_t* group_count;
+    int32_t* group_off;
+    int32_t* pair_count;
+    int32_t* tok_perm;
+    int32_t* tok_off;
+    int32_t* sorted_to_assign;
+    int32_t* assign_to_sorted;
+    void* x_sorted; /* ignored when fuse_gather */
+    void* y_sorted;
+    void* y_shared;
+    void* const* events;
+} moe_exports;
+
+/*
+ * The whole layer: route -> shuffle -> gather -> expert FFN (routed and
+ * shared) -> combine, enqueued on one stream.  out[T,H] in token order.
+ * ex may be NULL.  Workspace: moe_workspace_bytes(cfg).
+ */
+int32_t moe_forward(const moe_cfg* cfg, const moe_weights* w, const moe_inputs* in, void* out,
+                    const moe_exports* ex, void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

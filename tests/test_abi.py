@@ -1,0 +1,160 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every
+entry point include/moe.h declares, validates descriptions on the host and
+rejects bad arguments before anything is enqueued."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def m():
+    from token_routing_shuffle_amd import moe
+    if not os.path.exists(moe.LIB_PATH):
+        from token_routing_shuffle_amd import build
+        build.build()
+    moe.lib()
+    return moe
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int32_t|size_t|const char\*)\s+(moe_\w+)\s*\(", src, re.M)))
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted([
+        "moe_combine", "moe_expert_ffn", "moe_forward", "moe_last_error", "moe_route",
+        "moe_shuffle", "moe_validate", "moe_workspace_bytes"])
+
+
+def test_library_exports_every_declared_symbol(m):
+    lib = m.lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert sorted(m.EXPORTED) == declared_functions()
+
+
+def test_struct_layouts_match_header(m):
+    # moe_cfg: 20 int32/float fields, no padding; moe_exports: 17 pointers
+    assert ctypes.sizeof(m.moe_cfg) == 20 * 4
+    assert ctypes.sizeof(m.moe_weights) == 9 * 8
+    assert ctypes.sizeof(m.moe_inputs) == 3 * 8
+    assert ctypes.sizeof(m.moe_exports) == 17 * 8
+    hdr = open(os.path.join(ROOT, "include", "moe.h")).read()
+    body = hdr[hdr.index("typedef struct moe_cfg"):hdr.index("} moe_cfg;")]
+    names = re.findall(r"^\s*(?:int32_t|float)\s+(\w+);", body, re.M)
+    assert names == [f for f, _ in m.moe_cfg._fields_]
+
+
+def _cfgs(m):
+    from token_routing_shuffle_amd import workload as wl
+    return {n: m.make_cfg(c) for n, c in wl.CONFIGS.items()}
+
+
+def test_every_workload_config_validates(m):
+    for name, c in _cfgs(m).items():
+        assert m.moe_validate(c) == m.MOE_OK, (name, m.moe_last_error())
+        assert m.moe_workspace_bytes(c) > 0
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("E", 12, "MOE_ESHAPE"),            # E/P = 1.5
+    ("P", 3, "MOE_ESHAPE"),             # E % P != 0
+    ("k_max", 0, "MOE_ESHAPE"),
+    ("k_max", 65, "MOE_ESHAPE"),
+    ("H", 100, "MOE_ESHAPE"),           # bf16 needs H % 128
+    ("I", 1400, "MOE_ESHAPE"),          # bf16 needs I % 64
+    ("dtype", 7, "MOE_EDTYPE"),
+    ("gate", 5, "MOE_EDTYPE"),
+    ("T", -1, "MOE_ESHAPE"),
+    ("V", 0, "MOE_ESHAPE"),
+    ("n_pref", 65, "MOE_ESHAPE"),
+    ("ragged", 2, "MOE_EINVAL"),
+    ("E", 1024, "MOE_ESHAPE"),
+])
+def test_validate_rejects(m, field, value, code):
+    c = _cfgs(m)["dsv2lite"]
+    setattr(c, field, value)
+    assert m.moe_validate(c) == getattr(m, code)
+    assert m.moe_last_error()
+    assert m.moe_workspace_bytes(c) == 0
+
+
+def test_validate_sigmoid_group_rules(m):
+    base = _cfgs(m)["dsv3_prefill"]
+    assert m.moe_validate(base) == m.MOE_OK
+    for field, value in [("n_rgroups", 7), ("topk_rgroups", 9), ("topk_rgroups", 0),
+                         ("rgroup_topn", 0), ("rgroup_topn", 33)]:
+        c = _cfgs(m)["dsv3_prefill"]
+        setattr(c, field, value)
+        assert m.moe_validate(c) == m.MOE_ESHAPE, (field, value)
+    c = _cfgs(m)["dsv3_prefill"]
+    c.k_max, c.topk_rgroups = 64, 1          # one kept group of 32 experts < k
+    assert m.moe_validate(c) == m.MOE_ESHAPE
+
+
+def test_validate_null_cfg(m):
+    assert m.lib().moe_validate(None) == m.MOE_EINVAL
+
+
+def test_calls_reject_null_pointers_before_launching(m):
+    c = _cfgs(m)["dsv2lite"]
+    L = m.lib()
+    ref = ctypes.byref(c)
+    assert L.moe_route(ref, *([None] * 11), None, 0, None) == m.MOE_EINVAL
+    assert "NULL" in m.moe_last_error()
+    assert L.moe_shuffle(ref, *([None] * 15), None, 0, None) == m.MOE_EINVAL
+    assert L.moe_expert_ffn(ref, 0, *([None] * 7), 0, 64, None, None, 0, None) == m.MOE_EINVAL
+    assert L.moe_expert_ffn(ref, 9, *([None] * 7), 0, 64, None, None, 0, None) == m.MOE_EINVAL
+    assert L.moe_combine(ref, *([None] * 7)) == m.MOE_EINVAL
+    w, i = m.moe_weights(), m.moe_inputs()
+    assert L.moe_forward(ref, ctypes.byref(w), ctypes.byref(i), None, None, None, 0, None) == m.MOE_EINVAL
+
+
+def test_calls_reject_small_or_misaligned_workspace(m):
+    c = _cfgs(m)["tiny"]
+    L = m.lib()
+    need = m.moe_workspace_bytes(c)
+    fake = 1 << 40   # never dereferenced: the checks fail first
+    ptrs = [fake] * 15
+    rc = L.moe_shuffle(ctypes.byref(c), *ptrs, None, 0, None)
+    assert rc == m.MOE_EWORKSPACE
+    rc = L.moe_shuffle(ctypes.byref(c), *ptrs, fake + 8, need, None)
+    assert rc == m.MOE_EWORKSPACE and "aligned" in m.moe_last_error()
+    rc = L.moe_shuffle(ctypes.byref(c), *ptrs, fake, 256, None)
+    assert rc == m.MOE_EWORKSPACE
+    w = m.moe_weights(Wg=fake, slot_to_orig=fake, W13=fake, W2=fake, lut=fake)
+    i = m.moe_inputs(x=fake, tok=fake)
+    rc = L.moe_forward(ctypes.byref(c), ctypes.byref(w), ctypes.byref(i), fake, None, fake, need - 1, None)
+    assert rc == m.MOE_EWORKSPACE
+
+
+def test_calls_reject_misaligned_tensors(m):
+    c = _cfgs(m)["dsv2lite"]
+    L = m.lib()
+    fake = 1 << 40
+    rc = L.moe_route(ctypes.byref(c), fake + 2, fake, None, fake, fake, None, None, fake, fake,
+                     fake, None, None, 0, None)
+    assert rc == m.MOE_EINVAL and "aligned" in m.moe_last_error()
+
+
+def test_workspace_grows_with_tokens_and_shrinks_with_fused_gather(m):
+    from token_routing_shuffle_amd import workload as wl
+    c1 = m.make_cfg(wl.CONFIGS["qwen3"], T=1024)
+    c2 = m.make_cfg(wl.CONFIGS["qwen3"], T=2048)
+    c3 = m.make_cfg(wl.CONFIGS["qwen3"], T=2048, fuse_gather=1)
+    assert m.moe_workspace_bytes(c1) < m.moe_workspace_bytes(c2)
+    assert m.moe_workspace_bytes(c3) < m.moe_workspace_bytes(c2)
+    # the x_sorted buffer (A_max rows of H bf16) is what fusing the gather saves
+    assert m.moe_workspace_bytes(c2) - m.moe_workspace_bytes(c3) == 2048 * 8 * 2048 * 2
+
+
+def test_empty_layer_validates(m):
+    from token_routing_shuffle_amd import workload as wl
+    c = m.make_cfg(wl.CONFIGS["tiny"], T=0)
+    assert m.moe_validate(c) == m.MOE_OK

@@ -1,0 +1,92 @@
+// Combine: weighted sum of each token's expert outputs back in the original
+// token order (the Shuffled-Allgather's "restore the original order" step,
+// German summary, technical summary §2B; Japanese summary, technical overview
+// §2.2B), plus the shared-expert output.
+//
+// Gather-style and deterministic: one wave per token reads its k_t rows of
+// y_sorted through assign_to_sorted, accumulates w * y in fp32 in j order,
+// adds y_sh and writes the row once.  No atomics.
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+
+template <bool BF16>
+__global__ __launch_bounds__(kThreads) void k_combine(int T, int H, const void* __restrict__ ys,
+                                                      const int32_t* __restrict__ a2s,
+                                                      const int32_t* __restrict__ row_ptr,
+                                                      const float* __restrict__ topk_w,
+                                                      const void* __restrict__ ysh,
+                                                      void* __restrict__ out)
+{
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int l = threadIdx.x & 63;
+    if (t >= T) return;
+    constexpr int EPC = BF16 ? 8 : 4;  // elements per 16-byte chunk
+    const int nch = H / EPC;
+    const int a0 = row_ptr[t], a1 = row_ptr[t + 1];
+    for (int c = l; c < nch; c += 64) {
+        float acc[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
+        for (int a = a0; a < a1; ++a) {
+            const float wt = topk_w[a];
+            const size_t row = (size_t)a2s[a];
+            const u32x4_t v = ((const u32x4_t*)ys)[row * nch + c];
+            if constexpr (BF16) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[2 * q] = fmaf(wt, bf2f(v[q] & 0xffffu), acc[2 * q]);
+                    acc[2 * q + 1] = fmaf(wt, bf2f(v[q] >> 16), acc[2 * q + 1]);
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[q] = fmaf(wt, __uint_as_float(v[q]), acc[q]);
+            }
+        }
+        if (ysh != nullptr) {
+            const u32x4_t v = ((const u32x4_t*)ysh)[(size_t)t * nch + c];
+            if constexpr (BF16) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    acc[2 * q] += bf2f(v[q] & 0xffffu);
+                    acc[2 * q + 1] += bf2f(v[q] >> 16);
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) acc[q] += __uint_as_float(v[q]);
+            }
+        }
+        u32x4_t o;
+        if constexpr (BF16) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = pack_bf2(acc[2 * q], acc[2 * q + 1]);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) o[q] = __float_as_uint(acc[q]);
+        }
+        ((u32x4_t*)out)[(size_t)t * nch + c] = o;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const moe_cfg& c, const void* y_sorted, const int32_t* a2s,
+                          const int32_t* row_ptr, const float* topk_w, const void* y_sh,
+                          void* out, hipStream_t s)
+{
+    if (c.T == 0) return hipSuccess;
+    const dim3 grid(ceil_div(c.T, 4)), block(kThreads);
+    if (c.dtype == MOE_BF16)
+        hipLaunchKernelGGL(k_combine<true>, grid, block, 0, s, c.T, c.H, y_sorted, a2s, row_ptr,
+                           topk_w, y_sh, out);
+    else
+        hipLaunchKernelGGL(k_combine<false>, grid, block, 0, s, c.T, c.H, y_sorted, a2s, row_ptr,
+                           topk_w, y_sh, out);
+    return hipGetLastError();
+}
+
+}  // namespace moe

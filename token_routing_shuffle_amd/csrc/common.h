@@ -1,0 +1,141 @@
+// Device helpers shared by the libmoe kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define MOE_DEV __device__ __forceinline__
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// bf16 <-> fp32 (bf16 kept as raw uint16 bit patterns in memory)
+MOE_DEV float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+
+MOE_DEV uint32_t f2bf(float f)  // round to nearest even
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+MOE_DEV uint32_t pack_bf2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
+
+MOE_DEV int lane_id() { return (int)__lane_id(); }
+
+MOE_DEV uint64_t lanemask_lt() { return (1ull << lane_id()) - 1ull; }
+
+// Lanes (among `active`) whose `key` equals this lane's key; key < 2^nbits.
+// Multi-split by per-bit ballots: gfx950 has no match instruction.
+MOE_DEV uint64_t match_key(uint32_t key, int nbits, uint64_t active)
+{
+    uint64_t m = active;
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (key >> b) & 1u;
+        const uint64_t ones = __ballot(bit);
+        m &= bit ? ones : ~ones;
+    }
+    return m;
+}
+
+MOE_DEV float wave_sum(float v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+MOE_DEV float wave_max(float v)
+{
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+MOE_DEV int wave_incl_scan(int v)
+{
+    const int l = lane_id();
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int t = __shfl_up(v, o);
+        if (l >= o) v += t;
+    }
+    return v;
+}
+
+// Block-wide exclusive scan of one int per thread (blockDim.x <= 1024).
+// `smem` must hold 17 ints (16 wave prefixes + the total).  Returns the
+// exclusive prefix; *total = block sum.
+MOE_DEV int block_excl_scan(int v, int* smem, int* total)
+{
+    const int l = lane_id();
+    const int w = threadIdx.x >> 6;
+    const int nw = (blockDim.x + 63) >> 6;
+    int incl = wave_incl_scan(v);
+    if (l == 63) smem[w] = incl;
+    __syncthreads();
+    if (w == 0) {
+        int s = (l < nw) ? smem[l] : 0;
+        int si = wave_incl_scan(s);
+        if (l < nw) smem[l] = si - s;
+        if (l == nw - 1) smem[16] = si;
+    }
+    __syncthreads();
+    int r = incl - v + smem[w];
+    *total = smem[16];
+    __syncthreads();
+    return r;
+}
+
+MOE_DEV int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+// Own fp32 exp: Cody-Waite additive range reduction n = rint(x*log2 e),
+// r = x - n*ln2 with ln2 split into an fp32 high part and the fp32 rounding
+// of the remainder (one fused multiply-add each), exp(r) by the degree-7
+// Taylor polynomial in Horner form with fused multiply-adds, exact scaling
+// by 2^n.  Defined on [-87, 88] (normal results): 0 below, +inf above.
+// Bit-reproducible: every step is a single IEEE-rounded fp32 operation.
+MOE_DEV float cw_expf(float x)
+{
+#pragma clang fp contract(off)
+    constexpr double kLn2 = 0.69314718055994530942;
+    constexpr float ln2_hi = (float)kLn2;
+    constexpr float ln2_lo = (float)(kLn2 - (double)(float)kLn2);
+    constexpr float log2e = (float)1.44269504088896340736;
+    if (x != x) return x;
+    if (x < -87.0f) return 0.0f;
+    if (x > 88.0f) return __builtin_inff();
+    const float n = __builtin_rintf(x * log2e);
+    float r = __builtin_fmaf(-n, ln2_hi, x);
+    r = __builtin_fmaf(-n, ln2_lo, r);
+    float p = (float)(1.0 / 5040.0);
+    p = __builtin_fmaf(p, r, (float)(1.0 / 720.0));
+    p = __builtin_fmaf(p, r, (float)(1.0 / 120.0));
+    p = __builtin_fmaf(p, r, (float)(1.0 / 24.0));
+    p = __builtin_fmaf(p, r, (float)(1.0 / 6.0));
+    p = __builtin_fmaf(p, r, 0.5f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    p = __builtin_fmaf(p, r, 1.0f);
+    const float scale = __uint_as_float((uint32_t)((int)n + 127) << 23);
+    return p * scale;
+}
+
+MOE_DEV float cw_sigmoidf(float l)
+{
+#pragma clang fp contract(off)
+    const float e = cw_expf(-l);
+    const float d = 1.0f + e;
+    return 1.0f / d;
+}
+
+// Order-preserving map of a (non-NaN) float to uint32, -0 folded onto +0.
+MOE_DEV uint32_t ordered_key(float f)
+{
+    const float g = f + 0.0f;  // -0 + 0 = +0 under round-to-nearest
+    const uint32_t u = __float_as_uint(g);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}

@@ -1,0 +1,83 @@
+// Internal declarations shared by the libmoe translation units (host side).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+// Tokens per block of the histogram / scatter kernels of the shuffle.
+constexpr int kShuffleTPB = 512;
+
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+inline int ilog2(int v) { int r = 0; while ((1 << r) < v) ++r; return r; }
+
+// Workspace layout (byte offsets, 256-byte aligned sections).
+struct WsLayout {
+    size_t row_ptr, topk_slot, topk_w;            // route outputs (moe_forward)
+    size_t g_pred, hist, thist;                   // shuffle scratch
+    size_t expert_count, expert_off, group_count, group_off, pair_count;
+    size_t tok_perm, tok_off, s2a, a2s, row_tok;  // shuffle outputs / scratch
+    size_t x_sorted, h, h_sh, y_sorted, y_sh;     // expert FFN buffers
+    size_t shuffle_need, ffn_need, total;
+    int nb;                                       // shuffle blocks
+};
+
+WsLayout ws_layout(const moe_cfg& c);
+
+// --- launchers (no argument checks; callers validate) ---------------------
+hipError_t launch_row_ptr(const moe_cfg& c, const int32_t* k_tok, int32_t* row_ptr,
+                          hipStream_t s);
+hipError_t launch_route(const moe_cfg& c, const void* x, const void* Wg, const float* ebias,
+                        const int32_t* slot_to_orig, const int32_t* tok, const int32_t* pref,
+                        const int32_t* k_tok, const int32_t* row_ptr, int32_t* topk_slot,
+                        float* topk_w, float* logits, hipStream_t s);
+
+struct ShuffleOut {
+    int32_t *expert_count, *expert_off, *group_count, *group_off, *pair_count;
+    int32_t *tok_perm, *tok_off, *s2a, *a2s, *row_tok;
+    int32_t *g_pred, *hist, *thist;
+};
+hipError_t launch_shuffle(const moe_cfg& c, int nb, const int32_t* row_ptr,
+                          const int32_t* topk_slot, const int32_t* tok, const int32_t* lut,
+                          const ShuffleOut& o, hipStream_t s);
+hipError_t launch_gather(const moe_cfg& c, const void* x, const int32_t* row_ptr,
+                         const int32_t* a2s, void* x_sorted, hipStream_t s);
+hipError_t launch_row_tok(const moe_cfg& c, const int32_t* row_ptr, const int32_t* s2a,
+                          int32_t* row_tok, hipStream_t s);
+
+// One grouped-FFN launch pair covers the routed slots [e_begin, e_end)
+// (rows expert_off[e]..expert_off[e+1] of the sorted row space) and, when
+// sh_x != nullptr, the shared experts over all T rows.
+struct FfnArgs {
+    // routed part
+    int n_routed;                // e_end - e_begin (0: none)
+    const int32_t* expert_off;   // [E+1]; segment e uses [off[e_begin+i], off[e_begin+i+1])
+    int e_begin;
+    const void* xs;              // rows in sorted order, or nullptr -> x via row_tok
+    const void* x;               // [T,H]
+    const int32_t* row_tok;      // token of each sorted row (used when xs == nullptr)
+    const void* W13;             // [E,2I,H]
+    const void* W2;              // [E,H,I]
+    void* h;                     // [A_max, I] intermediate
+    void* y;                     // [A_max, H] output rows
+    int A_max;
+    // shared part (all T rows of x)
+    const void* sh_x;            // [T,H] or nullptr
+    const void* sh_W13;          // [2*Ish, H]
+    const void* sh_W2;           // [H, Ish]
+    void* sh_h;                  // [T, Ish]
+    void* sh_y;                  // [T, H]
+    int Ish;                     // n_shared * I_shared
+};
+hipError_t launch_ffn_up(const moe_cfg& c, const FfnArgs& a, hipStream_t s);
+hipError_t launch_ffn_down(const moe_cfg& c, const FfnArgs& a, hipStream_t s);
+
+hipError_t launch_combine(const moe_cfg& c, const void* y_sorted, const int32_t* a2s,
+                          const int32_t* row_ptr, const float* topk_w, const void* y_sh,
+                          void* out, hipStream_t s);
+
+}  // namespace moe

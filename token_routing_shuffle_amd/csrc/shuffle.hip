@@ -1,0 +1,306 @@
+// Shuffle: token->group lookup table and the dispatch metadata, as a stable
+// counting sort of the (token, expert) assignments by the key
+// (slot, predicted group, token), plus the token-level order by
+// (predicted group, token).
+//
+// The pages shuffle each token, before the MoE layer, to the device hosting
+// its predicted experts and put results back in the original order afterwards
+// (German summary, technical summary §2B; Japanese summary, technical overview
+// §2.2B), with the prediction read from a lightweight token->group table
+// (Japanese summary, §2.3).  On one GPU the "devices" are the P placement
+// groups of consecutive slots and no data moves between GPUs: the sort yields
+// expert-contiguous rows (each group's slots adjacent), per-slot / per-group
+// counts and offsets, the P x P would-be all-to-all matrix and the token
+// permutation.
+//
+// Three kernels: per-block LDS histograms, one single-block scan over the
+// (bucket, block) table in bucket-major order, and a scatter that ranks
+// equal buckets inside a wave with ballots (stable: blocks, waves, chunks and
+// lanes all follow assignment order).
+#include "common.h"
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kTPB = kShuffleTPB;      // tokens per block
+constexpr int kTPW = kTPB / 4;         // tokens per wave (scatter)
+constexpr int kMaxBuckets = 4096;      // E * P
+
+struct ShParams {
+    int T, E, P, V, nb, nbk, log2_epg, bucket_bits, group_bits, k_max;
+    const int32_t* row_ptr;
+    const int32_t* slot;
+    const int32_t* tok;
+    const int32_t* lut;
+    ShuffleOut o;
+};
+
+__global__ __launch_bounds__(kThreads) void k_hist(ShParams p)
+{
+    __shared__ int cnt[kMaxBuckets];
+    __shared__ int tcnt[64];
+    const int b = blockIdx.x;
+    const int t0 = b * kTPB, t1 = min(p.T, t0 + kTPB);
+    for (int i = threadIdx.x; i < p.nbk; i += kThreads) cnt[i] = 0;
+    if (threadIdx.x < 64) tcnt[threadIdx.x] = 0;
+    __syncthreads();
+    for (int t = t0 + threadIdx.x; t < t1; t += kThreads) {
+        const int v = clampi(p.tok[t], 0, p.V - 1);
+        const int g = clampi(p.lut[v], 0, p.P - 1);
+        p.o.g_pred[t] = g;
+        atomicAdd(&tcnt[g], 1);
+        const int a0 = p.row_ptr[t], a1 = p.row_ptr[t + 1];
+        for (int a = a0; a < a1; ++a) {
+            const int s = clampi(p.slot[a], 0, p.E - 1);
+            atomicAdd(&cnt[s * p.P + g], 1);
+        }
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < p.nbk; i += kThreads) p.o.hist[(size_t)i * p.nb + b] = cnt[i];
+    if (threadIdx.x < p.P) p.o.thist[threadIdx.x * p.nb + b] = tcnt[threadIdx.x];
+}
+
+// In-place exclusive scan of n ints (one block of 1024 threads); returns total.
+MOE_DEV int block_scan_inplace(int32_t* a, int n, int* smem)
+{
+    int carry = 0;
+    for (int base = 0; base < n; base += 4 * 1024) {
+        int v[4];
+        int sum = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int i = base + threadIdx.x * 4 + q;
+            v[q] = i < n ? a[i] : 0;
+            sum += v[q];
+        }
+        int total;
+        int run = carry + block_excl_scan(sum, smem, &total);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int i = base + threadIdx.x * 4 + q;
+            if (i < n) a[i] = run;
+            run += v[q];
+        }
+        carry += total;
+    }
+    return carry;
+}
+
+__global__ __launch_bounds__(1024) void k_scan(ShParams p)
+{
+    __shared__ int smem[17];
+    __shared__ int s_total;
+    const int n = p.nbk * p.nb;
+    const int A = block_scan_inplace(p.o.hist, n, smem);   // hist -> global offsets
+    const int T = block_scan_inplace(p.o.thist, p.P * p.nb, smem);
+    if (threadIdx.x == 0) s_total = A;
+    __syncthreads();
+    // bucket b = s*P + g starts at hist[b*nb]; the end of the last bucket is A
+    auto bstart = [&](int bk) { return bk < p.nbk ? p.o.hist[(size_t)bk * p.nb] : s_total; };
+    const int E = p.E, P = p.P, epg = E / P;
+    for (int s = threadIdx.x; s <= E; s += 1024) {
+        const int off = bstart(s * P);
+        p.o.expert_off[s] = off;
+        if (s < E) p.o.expert_count[s] = bstart((s + 1) * P) - off;
+    }
+    for (int g = threadIdx.x; g <= P; g += 1024) {
+        const int off = bstart(g * epg * P);
+        p.o.group_off[g] = off;
+        if (g < P) p.o.group_count[g] = bstart((g + 1) * epg * P) - off;
+        p.o.tok_off[g] = g < P ? p.o.thist[g * p.nb] : T;
+    }
+    // pair_count[pg * P + g]: predicted group pg, expert group g
+    for (int i = threadIdx.x; i < P * P; i += 1024) {
+        const int pg = i / P, g = i % P;
+        int c = 0;
+        for (int s = g * epg; s < (g + 1) * epg; ++s) c += bstart(s * P + pg + 1) - bstart(s * P + pg);
+        p.o.pair_count[i] = c;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void k_scatter(ShParams p)
+{
+    __shared__ int base[4][kMaxBuckets];
+    __shared__ int tbase[4][64];
+    __shared__ int s_rp[kTPB + 1];
+    const int b = blockIdx.x;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int t0 = b * kTPB, t1 = min(p.T, t0 + kTPB);
+    const int nt = t1 - t0;
+    const int tw0 = min(t1, t0 + w * kTPW), tw1 = min(t1, t0 + (w + 1) * kTPW);
+    const int nbk = p.nbk, P = p.P;
+
+    for (int i = threadIdx.x; i < 4 * nbk; i += kThreads) base[i / nbk][i % nbk] = 0;
+    for (int i = threadIdx.x; i < 4 * 64; i += kThreads) tbase[i / 64][i % 64] = 0;
+    for (int i = threadIdx.x; i <= nt; i += kThreads) s_rp[i] = p.row_ptr[t0 + i];
+    __syncthreads();
+    // per-wave counts
+    for (int t = tw0 + l; t < tw1; t += 64) {
+        const int g = p.o.g_pred[t];
+        atomicAdd(&tbase[w][g], 1);
+        for (int a = s_rp[t - t0]; a < s_rp[t - t0 + 1]; ++a)
+            atomicAdd(&base[w][clampi(p.slot[a], 0, p.E - 1) * P + g], 1);
+    }
+    __syncthreads();
+    // counts -> starting positions: block offset + earlier waves' counts
+    for (int i = threadIdx.x; i < nbk; i += kThreads) {
+        int run = p.o.hist[(size_t)i * p.nb + b];
+        for (int q = 0; q < 4; ++q) {
+            const int c = base[q][i];
+            base[q][i] = run;
+            run += c;
+        }
+    }
+    if (threadIdx.x < P) {
+        int run = p.o.thist[threadIdx.x * p.nb + b];
+        for (int q = 0; q < 4; ++q) {
+            const int c = tbase[q][threadIdx.x];
+            tbase[q][threadIdx.x] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+
+    // assignments of this wave's tokens, 64 at a time, in assignment order
+    const int a_begin = s_rp[tw0 - t0], a_end = s_rp[tw1 - t0];
+    for (int c0 = a_begin; c0 < a_end; c0 += 64) {
+        const int a = c0 + l;
+        const bool valid = a < a_end;
+        uint32_t bucket = 0;
+        int t = 0;
+        if (valid) {
+            // token of assignment a: last i with s_rp[i] <= a, within this wave's tokens
+            int lo = tw0 - t0, hi = tw1 - t0 - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (s_rp[mid] <= a) lo = mid; else hi = mid - 1;
+            }
+            t = t0 + lo;
+            bucket = (uint32_t)(clampi(p.slot[a], 0, p.E - 1) * P + p.o.g_pred[t]);
+        }
+        const uint64_t act = __ballot(valid);
+        const uint64_t peers = match_key(bucket, p.bucket_bits, act);
+        if (valid) {
+            const int rank = __popcll(peers & lanemask_lt());
+            const int dest = base[w][bucket] + rank;
+            p.o.s2a[dest] = a;
+            p.o.a2s[a] = dest;
+            if (p.o.row_tok) p.o.row_tok[dest] = t;
+            // the highest lane of each bucket advances its running position
+            if ((peers >> l) == 1ull) base[w][bucket] = dest + 1;
+        }
+    }
+    // tokens of this wave in token order -> tok_perm
+    for (int c0 = tw0; c0 < tw1; c0 += 64) {
+        const int t = c0 + l;
+        const bool valid = t < tw1;
+        const uint32_t g = valid ? (uint32_t)p.o.g_pred[t] : 0u;
+        const uint64_t act = __ballot(valid);
+        const uint64_t peers = match_key(g, p.group_bits, act);
+        if (valid) {
+            const int dest = tbase[w][g] + __popcll(peers & lanemask_lt());
+            p.o.tok_perm[dest] = t;
+            if ((peers >> l) == 1ull) tbase[w][g] = dest + 1;
+        }
+    }
+}
+
+// x_sorted[assign_to_sorted[a]] = x[t] for every assignment a of token t:
+// each x row is read once and written k_t times.  One wave per token, 16-byte
+// chunks.
+__global__ __launch_bounds__(kThreads) void k_gather(int T, int row_bytes,
+                                                     const char* __restrict__ x,
+                                                     const int32_t* __restrict__ row_ptr,
+                                                     const int32_t* __restrict__ a2s,
+                                                     char* __restrict__ xs)
+{
+    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int l = threadIdx.x & 63;
+    if (t >= T) return;
+    const int nch = row_bytes >> 4;
+    const int a0 = row_ptr[t], a1 = row_ptr[t + 1];
+    const u32x4_t* src = (const u32x4_t*)(x + (size_t)t * row_bytes);
+    for (int c = l; c < nch; c += 4 * 64) {
+        u32x4_t v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (c + q * 64 < nch) v[q] = src[c + q * 64];
+        for (int a = a0; a < a1; ++a) {
+            u32x4_t* dst = (u32x4_t*)(xs + (size_t)a2s[a] * row_bytes);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (c + q * 64 < nch) dst[c + q * 64] = v[q];
+        }
+    }
+}
+
+// row_tok[s] = token of assignment s2a[s] (binary search in row_ptr).
+__global__ __launch_bounds__(kThreads) void k_row_tok(int T, int A_max,
+                                                      const int32_t* __restrict__ row_ptr,
+                                                      const int32_t* __restrict__ s2a,
+                                                      int32_t* __restrict__ row_tok)
+{
+    const int s = blockIdx.x * kThreads + threadIdx.x;
+    const int A = row_ptr[T];
+    if (s >= A || s >= A_max) return;
+    const int a = s2a[s];
+    int lo = 0, hi = T - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (row_ptr[mid] <= a) lo = mid; else hi = mid - 1;
+    }
+    row_tok[s] = lo;
+}
+
+}  // namespace
+
+hipError_t launch_shuffle(const moe_cfg& c, int nb, const int32_t* row_ptr,
+                          const int32_t* topk_slot, const int32_t* tok, const int32_t* lut,
+                          const ShuffleOut& o, hipStream_t s)
+{
+    ShParams p;
+    p.T = c.T;
+    p.E = c.E;
+    p.P = c.P;
+    p.V = c.V;
+    p.nb = nb;
+    p.nbk = c.E * c.P;
+    p.log2_epg = ilog2(c.E / c.P);
+    p.bucket_bits = ilog2(p.nbk);
+    p.group_bits = ilog2(c.P);
+    p.k_max = c.k_max;
+    p.row_ptr = row_ptr;
+    p.slot = topk_slot;
+    p.tok = tok;
+    p.lut = lut;
+    p.o = o;
+    // the histogram kernel also runs for T == 0 so the table it writes is zero
+    hipLaunchKernelGGL(k_hist, dim3(nb), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, p);
+    if (c.T > 0) hipLaunchKernelGGL(k_scatter, dim3(nb), dim3(kThreads), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather(const moe_cfg& c, const void* x, const int32_t* row_ptr,
+                         const int32_t* a2s, void* x_sorted, hipStream_t s)
+{
+    if (c.T == 0) return hipSuccess;
+    const int esz = c.dtype == MOE_BF16 ? 2 : 4;
+    hipLaunchKernelGGL(k_gather, dim3(ceil_div(c.T, 4)), dim3(kThreads), 0, s, c.T, c.H * esz,
+                       (const char*)x, row_ptr, a2s, (char*)x_sorted);
+    return hipGetLastError();
+}
+
+hipError_t launch_row_tok(const moe_cfg& c, const int32_t* row_ptr, const int32_t* s2a,
+                          int32_t* row_tok, hipStream_t s)
+{
+    const int A_max = c.T * c.k_max;
+    if (A_max == 0) return hipSuccess;
+    hipLaunchKernelGGL(k_row_tok, dim3(ceil_div(A_max, kThreads)), dim3(kThreads), 0, s, c.T,
+                       A_max, row_ptr, s2a, row_tok);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,75 @@
+"""Offline tables of a layer: placement-ordered weights and the token->group
+lookup table.
+
+Sem-MoE prepares both before serving (Japanese summary, technical overview
+§2.2A and §2.3; German summary, technical summary §2A):
+  * the expert placement is applied by shuffling the gate matrix's columns
+    (and moving each expert's weights with it) — ``place`` reorders every
+    per-expert tensor into slot order, slot = placement position;
+  * a lightweight table maps each token ID to the placement group that its
+    experts most often live in, learned by profiling — ``profile_lut`` routes
+    a profiling draw through the library's own moe_route on the GPU and keeps,
+    for each token ID, the group that received most of its assignments (ties
+    to the lower group; IDs never seen map to v mod P).
+Neither runs on the per-layer hot path.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import moe
+
+
+def place(w: dict, slot_to_orig: np.ndarray, device) -> dict:
+    """Per-expert tensors in slot order: out[s] = in[slot_to_orig[s]]."""
+    idx = torch.as_tensor(np.asarray(slot_to_orig, np.int64), device=device)
+    out = {}
+    for name in ("Wg", "W13", "W2"):
+        out[name] = w[name].to(device).index_select(0, idx).contiguous()
+    for name in ("Wsh13", "Wsh2"):
+        out[name] = None if w.get(name) is None else w[name].to(device).contiguous()
+    return out
+
+
+def device_layer(cfg, tables, w: dict, lut: np.ndarray, device="cuda") -> dict:
+    """Every device tensor moe_forward needs, keyed like moe_weights."""
+    d = place(w, tables.slot_to_orig, device)
+    d["slot_to_orig"] = torch.as_tensor(tables.slot_to_orig, device=device)
+    d["ebias"] = None
+    if tables.ebias is not None:
+        d["ebias"] = torch.as_tensor(tables.ebias[tables.slot_to_orig], device=device)
+    d["lut"] = torch.as_tensor(np.asarray(lut, np.int32), device=device)
+    d["pref"] = None if tables.pref is None else torch.as_tensor(tables.pref, device=device)
+    return d
+
+
+def profile_lut(cfg, dev: dict, prof_x: torch.Tensor, prof_tok: np.ndarray,
+                chunk: int = 16384) -> np.ndarray:
+    """Token->group table from routing a profiling draw with moe_route."""
+    device = prof_x.device
+    n = prof_x.shape[0]
+    E, P = cfg.E, cfg.P
+    epg = E // P
+    counts = np.zeros((cfg.V, P), np.int64)
+    tok_all = torch.as_tensor(np.asarray(prof_tok, np.int32), device=device)
+    for s in range(0, n, chunk):
+        m = min(chunk, n - s)
+        c = moe.make_cfg(cfg, T=m)
+        k_tok = None
+        if cfg.ragged:
+            k_tok = torch.full((m,), cfg.k, dtype=torch.int32, device=device)
+        row_ptr = torch.empty(m + 1, dtype=torch.int32, device=device)
+        slots = torch.empty(m * cfg.k, dtype=torch.int32, device=device)
+        wts = torch.empty(m * cfg.k, dtype=torch.float32, device=device)
+        moe.moe_route(c, prof_x[s:s + m], dev["Wg"], dev.get("ebias"), dev["slot_to_orig"],
+                      tok_all[s:s + m], dev.get("pref"), k_tok, row_ptr, slots, wts)
+        rp = row_ptr.cpu().numpy()
+        sl = slots.cpu().numpy()[: rp[-1]]
+        t_of_a = np.repeat(np.arange(m), np.diff(rp))
+        v = np.asarray(prof_tok[s:s + m])[t_of_a]
+        np.add.at(counts, (v, sl // epg), 1)
+    lut = np.argmax(counts, axis=1).astype(np.int32)
+    unseen = counts.sum(axis=1) == 0
+    lut[unseen] = (np.arange(cfg.V)[unseen] % P).astype(np.int32)
+    return lut
