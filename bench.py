@@ -33,6 +33,9 @@ def parse():
     ap.add_argument("--fuse-gather", type=int, default=int(os.environ.get("MOE_BENCH_FUSE_GATHER", "1")))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=256, help="tokens in the oracle's timed sample")
+    ap.add_argument("--copy-calib-mb", type=int, default=0,
+                    help="after the timed steps, run one plain device copy of this many MiB "
+                         "(reference point for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -115,6 +118,14 @@ def main():
         v = [ev_sets[i][2 * si].elapsed_time(ev_sets[i][2 * si + 1]) for i in range(args.steps)]
         stage_ms[name] = float(np.mean(v))
 
+    if args.copy_calib_mb > 0:
+        n = args.copy_calib_mb << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     A = int(row_ptr[T].item())
     pc = pair.cpu().numpy().reshape(P, P)
     counts = ecount.cpu().numpy()

@@ -32,19 +32,32 @@ __global__ __launch_bounds__(kThreads) void k_combine(int T, int H, const void* 
         float acc[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
-        for (int a = a0; a < a1; ++a) {
-            const float wt = topk_w[a];
-            const size_t row = (size_t)a2s[a];
-            const u32x4_t v = ((const u32x4_t*)ys)[row * nch + c];
-            if constexpr (BF16) {
+        // rows of up to 8 assignments are loaded before they are summed, so
+        // their memory latencies overlap; the sum stays in j order
+        for (int a8 = a0; a8 < a1; a8 += 8) {
+            u32x4_t v[8];
+            float wt[8];
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    acc[2 * q] = fmaf(wt, bf2f(v[q] & 0xffffu), acc[2 * q]);
-                    acc[2 * q + 1] = fmaf(wt, bf2f(v[q] >> 16), acc[2 * q + 1]);
+            for (int j = 0; j < 8; ++j) {
+                if (a8 + j < a1) {
+                    wt[j] = topk_w[a8 + j];
+                    v[j] = ((const u32x4_t*)ys)[(size_t)a2s[a8 + j] * nch + c];
                 }
-            } else {
+            }
 #pragma unroll
-                for (int q = 0; q < 4; ++q) acc[q] = fmaf(wt, __uint_as_float(v[q]), acc[q]);
+            for (int j = 0; j < 8; ++j) {
+                if (a8 + j < a1) {
+                    if constexpr (BF16) {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            acc[2 * q] = fmaf(wt[j], bf2f(v[j][q] & 0xffffu), acc[2 * q]);
+                            acc[2 * q + 1] = fmaf(wt[j], bf2f(v[j][q] >> 16), acc[2 * q + 1]);
+                        }
+                    } else {
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) acc[q] = fmaf(wt[j], __uint_as_float(v[j][q]), acc[q]);
+                    }
+                }
             }
         }
         if (ysh != nullptr) {

@@ -42,18 +42,90 @@ MOE_DEV uint64_t match_key(uint32_t key, int nbits, uint64_t active)
     return m;
 }
 
+// Cross-lane moves through DPP (no LDS round trip).  Control codes:
+// quad_perm [1,0,3,2] = 0xB1 (lane ^ 1), quad_perm [2,3,0,1] = 0x4E (lane ^ 2),
+// row_half_mirror = 0x141 (i <-> 7-i in 8 lanes), row_mirror = 0x140
+// (i <-> 15-i in 16 lanes).  After the four steps every lane of a 16-lane
+// row holds the row's result; the four rows are then combined through
+// readlane in a fixed order, so every lane gets the same, deterministic
+// value.  All 64 lanes must be active.
+template <int CTRL>
+MOE_DEV uint32_t dpp_u32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+MOE_DEV float dpp_f32(float v)
+{
+    return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+
+MOE_DEV float readlane_f32(float v, int lane)
+{
+    return __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v), lane));
+}
+
+MOE_DEV uint32_t readlane_u32(uint32_t v, int lane)
+{
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
+}
+
 MOE_DEV float wave_sum(float v)
 {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-    return v;
+    v += dpp_f32<0xB1>(v);
+    v += dpp_f32<0x4E>(v);
+    v += dpp_f32<0x141>(v);
+    v += dpp_f32<0x140>(v);
+    return ((readlane_f32(v, 0) + readlane_f32(v, 16)) + readlane_f32(v, 32)) + readlane_f32(v, 48);
 }
 
 MOE_DEV float wave_max(float v)
 {
+    v = fmaxf(v, dpp_f32<0xB1>(v));
+    v = fmaxf(v, dpp_f32<0x4E>(v));
+    v = fmaxf(v, dpp_f32<0x141>(v));
+    v = fmaxf(v, dpp_f32<0x140>(v));
+    return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)),
+                 fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
+}
+
+// Arg-best over the wave of (uk desc, id asc), carrying a payload s.
+MOE_DEV bool beats(uint32_t uk, uint32_t id, uint32_t ouk, uint32_t oid)
+{
+    return ouk > uk || (ouk == uk && oid < id);
+}
+
+template <int CTRL>
+MOE_DEV void argbest_step(uint32_t& uk, uint32_t& id, uint32_t& s)
+{
+    const uint32_t ouk = dpp_u32<CTRL>(uk), oid = dpp_u32<CTRL>(id), os = dpp_u32<CTRL>(s);
+    if (beats(uk, id, ouk, oid)) {
+        uk = ouk;
+        id = oid;
+        s = os;
+    }
+}
+
+MOE_DEV void wave_argbest(uint32_t& uk, uint32_t& id, uint32_t& s)
+{
+    argbest_step<0xB1>(uk, id, s);
+    argbest_step<0x4E>(uk, id, s);
+    argbest_step<0x141>(uk, id, s);
+    argbest_step<0x140>(uk, id, s);
+    uint32_t buk = readlane_u32(uk, 0), bid = readlane_u32(id, 0), bs = readlane_u32(s, 0);
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-    return v;
+    for (int r = 16; r < 64; r += 16) {
+        const uint32_t ouk = readlane_u32(uk, r), oid = readlane_u32(id, r);
+        if (beats(buk, bid, ouk, oid)) {
+            buk = ouk;
+            bid = oid;
+            bs = readlane_u32(s, r);
+        }
+    }
+    uk = buk;
+    id = bid;
+    s = bs;
 }
 
 MOE_DEV int wave_incl_scan(int v)

@@ -15,8 +15,11 @@
 // reused from that XCD's L2.
 //
 // Tile 128 x 128 x 64, 256 threads (2 x 2 waves of 64 x 64), MFMA
-// 16x16x32 bf16, LDS double buffer with a padded row stride (72 elements) to
-// spread ds_read_b128 over the banks.
+// 16x16x32 bf16, LDS double buffer.  LDS rows are 64 bf16 (128 bytes, eight
+// 16-byte chunks) stored with an XOR swizzle: chunk c of row r sits at chunk
+// position c ^ (r & 7).  Measured on gfx950, both the loader's row-wise
+// ds_write_b128 and the MFMA fragment ds_read_b128 (16 rows x one chunk) are
+// then free of bank conflicts, unlike a padded row stride.
 #include "common.h"
 #include "internal.h"
 
@@ -24,7 +27,7 @@ namespace moe {
 namespace {
 
 constexpr int BM = 128, BN = 128, BK = 64;
-constexpr int LDSK = BK + 8;
+constexpr int LDSK = BK;   // no padding: XOR-swizzled chunks
 constexpr int kThreads = 256;
 constexpr int kMaxSeg = 516;
 
@@ -48,10 +51,13 @@ struct GemmParams {
 
 MOE_DEV float silu(float g) { return g / (1.0f + expf(-g)); }
 
+template <bool UP>
 __global__ __launch_bounds__(kThreads, 2) void k_grouped_gemm(GemmParams p)
 {
-    __shared__ __attribute__((aligned(16))) uint16_t As[2][BM][LDSK];
-    __shared__ __attribute__((aligned(16))) uint16_t Bs[2][BN][LDSK];
+    // LDS: two stages of [A tile | B tile] (XOR-swizzled 128-byte rows);
+    // reused after the K loop to stage the output tile for 16-byte stores.
+    constexpr int kStage = (BM + BN) * LDSK;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kStage];
     __shared__ int s_pref[kMaxSeg + 1];
     __shared__ int s_row0[kMaxSeg];
     __shared__ int s_cnt[kMaxSeg];
@@ -75,11 +81,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_gemm(GemmParams p)
                     const int e = p.e_begin + i;
                     row0 = p.expert_off[e];
                     cnt = p.expert_off[e + 1] - row0;
-                    nt = p.up ? p.N / 64 : p.N / BN;
+                    nt = UP ? p.N / 64 : p.N / BN;
                 } else {
                     row0 = 0;
                     cnt = p.T;
-                    nt = p.up ? p.shN / 64 : p.shN / BN;
+                    nt = UP ? p.shN / 64 : p.shN / BN;
                 }
                 s_row0[i] = row0;
                 s_cnt[i] = cnt;
@@ -126,7 +132,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_gemm(GemmParams p)
         // ---- operand row pointers (rows past the segment end repeat its last row)
         const uint16_t* ap[4];
         const uint16_t* bp[4];
-        const uint16_t* Bseg = shared ? p.shB : p.B + (size_t)(p.e_begin + seg) * (p.up ? 2 * (size_t)N : (size_t)N) * K;
+        const uint16_t* Bseg = shared ? p.shB : p.B + (size_t)(p.e_begin + seg) * (UP ? 2 * (size_t)N : (size_t)N) * K;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int r = lr + 32 * q;
@@ -140,7 +146,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_gemm(GemmParams p)
                 arow = p.X + (size_t)p.row_tok[gr] * K;
             ap[q] = arow + lc;
             int brow;
-            if (p.up) {
+            if (UP) {
                 const int n0 = ntile * 64;
                 brow = r < 64 ? n0 + r : N + n0 + (r - 64);
             } else {
@@ -155,41 +161,46 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_gemm(GemmParams p)
 #pragma unroll
             for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        u32x4_t ra[4], rb[4];
+        // global -> register stages, two k-tiles ahead of the MFMAs
+        u32x4_t r0a[4], r0b[4], r1a[4], r1b[4];
+        auto gload = [&](u32x4_t* ra, u32x4_t* rb, int kt) {
+            const int ko = kt * BK;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            ra[q] = *(const u32x4_t*)(ap[q]);
-            rb[q] = *(const u32x4_t*)(bp[q]);
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            *(u32x4_t*)&As[0][lr + 32 * q][lc] = ra[q];
-            *(u32x4_t*)&Bs[0][lr + 32 * q][lc] = rb[q];
-        }
-        __syncthreads();
-
-        const int KT = K / BK;
-        for (int kt = 0; kt < KT; ++kt) {
-            const int buf = kt & 1;
-            if (kt + 1 < KT) {
-                const int ko = (kt + 1) * BK;
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    ra[q] = *(const u32x4_t*)(ap[q] + ko);
-                    rb[q] = *(const u32x4_t*)(bp[q] + ko);
-                }
+            for (int q = 0; q < 4; ++q) {
+                ra[q] = *(const u32x4_t*)(ap[q] + ko);
+                rb[q] = *(const u32x4_t*)(bp[q] + ko);
             }
+        };
+        auto lstore = [&](const u32x4_t* ra, const u32x4_t* rb, int buf) {
+            uint16_t* As = smem + buf * kStage;
+            uint16_t* Bs = As + BM * LDSK;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int row = lr + 32 * q;
+                const int pos = (((lc >> 3) ^ (row & 7)) << 3);
+                *(u32x4_t*)&As[row * LDSK + pos] = ra[q];
+                *(u32x4_t*)&Bs[row * LDSK + pos] = rb[q];
+            }
+        };
+        auto compute = [&](int buf) {
+            const uint16_t* As = smem + buf * kStage;
+            const uint16_t* Bs = As + BM * LDSK;
 #pragma unroll
             for (int kk = 0; kk < BK; kk += 32) {
                 bf16x8_t af[4], bfr[4];
 #pragma unroll
-                for (int rt = 0; rt < 4; ++rt)
-                    af[rt] = *(const bf16x8_t*)&As[buf][wm * 64 + rt * 16 + (l & 15)][kk + (l >> 4) * 8];
+                for (int rt = 0; rt < 4; ++rt) {
+                    const int row = wm * 64 + rt * 16 + (l & 15);
+                    const int pos = ((((kk >> 3) + (l >> 4)) ^ (row & 7)) << 3);
+                    af[rt] = *(const bf16x8_t*)&As[row * LDSK + pos];
+                }
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct) {
-                    const int cb = p.up ? ((ct < 2) ? wn * 32 + ct * 16 : 64 + wn * 32 + (ct - 2) * 16)
-                                        : wn * 64 + ct * 16;
-                    bfr[ct] = *(const bf16x8_t*)&Bs[buf][cb + (l & 15)][kk + (l >> 4) * 8];
+                    const int cb = UP ? ((ct < 2) ? wn * 32 + ct * 16 : 64 + wn * 32 + (ct - 2) * 16)
+                                      : wn * 64 + ct * 16;
+                    const int row = cb + (l & 15);
+                    const int pos = ((((kk >> 3) + (l >> 4)) ^ (row & 7)) << 3);
+                    bfr[ct] = *(const bf16x8_t*)&Bs[row * LDSK + pos];
                 }
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt)
@@ -197,20 +208,35 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_gemm(GemmParams p)
                     for (int ct = 0; ct < 4; ++ct)
                         acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[rt], bfr[ct], acc[rt][ct], 0, 0, 0);
             }
-            if (kt + 1 < KT) {
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    *(u32x4_t*)&As[buf ^ 1][lr + 32 * q][lc] = ra[q];
-                    *(u32x4_t*)&Bs[buf ^ 1][lr + 32 * q][lc] = rb[q];
-                }
-            }
+        };
+
+        const int KT = K / BK;
+        gload(r0a, r0b, 0);
+        lstore(r0a, r0b, 0);
+        if (KT > 1) gload(r1a, r1b, 1);
+        if (KT > 2) gload(r0a, r0b, 2);
+        __syncthreads();
+        // invariant at even kt: LDS buf 0 holds tile kt, r1 holds kt+1, r0 holds kt+2
+        for (int kt = 0; kt < KT; kt += 2) {
+            compute(0);
+            if (kt + 1 < KT) lstore(r1a, r1b, 1);
+            if (kt + 3 < KT) gload(r1a, r1b, kt + 3);
             __syncthreads();
+            if (kt + 1 < KT) {
+                compute(1);
+                if (kt + 2 < KT) lstore(r0a, r0b, 0);
+                if (kt + 4 < KT) gload(r0a, r0b, kt + 4);
+                __syncthreads();
+            }
         }
 
-        // ---- epilogue: D lane layout: column (l & 15), rows 4*(l >> 4) + v
+        // ---- epilogue: D lane layout: column (l & 15), rows 4*(l >> 4) + v.
+        // Stage the bf16 tile in LDS, then write 16-byte row chunks.
         uint16_t* Cseg = shared ? p.shC : p.C;
-        if (p.up) {
-            const int n0 = ntile * 64;
+        constexpr int CW = UP ? 64 : BN;   // output columns of the tile
+        constexpr int CS = CW + 8;         // padded LDS row stride
+        uint16_t* Cs = smem;
+        if (UP) {
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -218,11 +244,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_gemm(GemmParams p)
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
                         const int row = wm * 64 + rt * 16 + (l >> 4) * 4 + v;
-                        if (row < rows) {
-                            const float g = acc[rt][c][v], u = acc[rt][c + 2][v];
-                            const int n = n0 + wn * 32 + c * 16 + (l & 15);
-                            Cseg[(size_t)(row0 + m0 + row) * N + n] = (uint16_t)f2bf(silu(g) * u);
-                        }
+                        const float g = acc[rt][c][v], u = acc[rt][c + 2][v];
+                        Cs[row * CS + wn * 32 + c * 16 + (l & 15)] = (uint16_t)f2bf(silu(g) * u);
                     }
         } else {
 #pragma unroll
@@ -232,12 +255,21 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_gemm(GemmParams p)
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
                         const int row = wm * 64 + rt * 16 + (l >> 4) * 4 + v;
-                        if (row < rows) {
-                            const int n = ntile * BN + wn * 64 + ct * 16 + (l & 15);
-                            Cseg[(size_t)(row0 + m0 + row) * N + n] = (uint16_t)f2bf(acc[rt][ct][v]);
-                        }
+                        Cs[row * CS + wn * 64 + ct * 16 + (l & 15)] = (uint16_t)f2bf(acc[rt][ct][v]);
                     }
         }
+        __syncthreads();
+        constexpr int CPR = CW / 8;        // 16-byte chunks per row
+        const int n_out = UP ? ntile * 64 : ntile * BN;
+#pragma unroll
+        for (int q = 0; q < (BM * CPR) / kThreads; ++q) {
+            const int idx = tid + q * kThreads;
+            const int row = idx / CPR, ch = idx % CPR;
+            if (row < rows)
+                *(u32x4_t*)&Cseg[(size_t)(row0 + m0 + row) * N + n_out + ch * 8] =
+                    *(const u32x4_t*)&Cs[row * CS + ch * 8];
+        }
+        __syncthreads();
     }
 }
 
@@ -353,7 +385,10 @@ hipError_t launch_gemm(const moe_cfg& c, const FfnArgs& a, bool up, hipStream_t 
     if (ub == 0) return hipSuccess;
     long long grid = std::min<long long>(ub, 2LL * num_cus());
     grid = (grid + 7) / 8 * 8;
-    hipLaunchKernelGGL(k_grouped_gemm, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+    if (up)
+        hipLaunchKernelGGL(k_grouped_gemm<true>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL(k_grouped_gemm<false>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
     return hipGetLastError();
 }
 

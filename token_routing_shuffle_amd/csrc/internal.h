@@ -10,7 +10,7 @@
 namespace moe {
 
 // Tokens per block of the histogram / scatter kernels of the shuffle.
-constexpr int kShuffleTPB = 512;
+constexpr int kShuffleTPB = 256;
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 inline int ilog2(int v) { int r = 0; while ((1 << r) < v) ++r; return r; }

@@ -86,6 +86,8 @@ __global__ __launch_bounds__(kThreads) void k_route(RouteParams p)
     __shared__ int s_o2s[EP];
     __shared__ float s_key[4][EP];
     __shared__ float s_gs[4][64];
+    constexpr int kSK = NTW == 1 ? 4 : (NTW == 2 ? 2 : 1);
+    __shared__ float s_part[kSK > 1 ? kSK : 1][kBM][kSK > 1 ? EP : 1];
 
     const int tid = threadIdx.x;
     const int w = tid >> 6;
@@ -93,7 +95,32 @@ __global__ __launch_bounds__(kThreads) void k_route(RouteParams p)
     const int t0 = blockIdx.x * kBM;
     const int T = p.T, H = p.H, E = p.E;
 
+    __shared__ int s_rp[kBM], s_kt[kBM];
     for (int s = tid; s < EP; s += kThreads) s_s2o[s] = s < E ? clampi(p.s2o[s], 0, E - 1) : s;
+    if (tid < kBM) {
+        const int t = t0 + tid;
+        s_rp[tid] = t < T ? p.row_ptr[t] : 0;
+        s_kt[tid] = t >= T ? 0 : (p.ragged ? clampi(p.k_tok[t], 0, p.k_max) : p.k_max);
+    }
+    // the affinity table is read before the GEMM so its latency overlaps it
+    const bool do_bias = p.pref != nullptr && p.aff_bias != 0.0f && p.n_pref > 0;
+    const int np = p.n_pref;
+    int pre_o[4], pre_row[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        pre_o[q] = -1;
+        pre_row[q] = 0;
+        const int idx = tid + q * kThreads;
+        if (do_bias && idx < kBM * np) {
+            const int row = idx / np, j = idx % np;
+            const int t = t0 + row;
+            if (t < T) {
+                const int v = clampi(p.tok[t], 0, p.V - 1);
+                pre_o[q] = p.pref[(size_t)v * np + j];
+                pre_row[q] = row;
+            }
+        }
+    }
     __syncthreads();
     for (int s = tid; s < E; s += kThreads) s_o2s[s_s2o[s]] = s;
 
@@ -101,36 +128,73 @@ __global__ __launch_bounds__(kThreads) void k_route(RouteParams p)
     if constexpr (BF16) {
         // MFMA 16x16x32 bf16.  Lane l feeds token row (l & 15) and expert
         // column (l & 15) of its tile; its 4-lane group kg = l >> 4 owns the
-        // contiguous k-range [16kg, 16kg+16) of every 64-wide step, split over
-        // two MFMAs (A and B use the same k assignment, so the contraction
-        // is complete; only the summation order is the hardware's).
+        // contiguous k-range [16kg, 16kg+16) of every 64-wide chunk, split over
+        // two MFMAs (A and B use the same k assignment, so the contraction is
+        // complete; only the summation order is the hardware's).
+        // Waves split the chunks (SK ways, interleaved) and the column tiles
+        // (SN ways); partial sums over the K split are added in wave order.
+        constexpr int SK = NTW == 1 ? 4 : (NTW == 2 ? 2 : 1);
+        constexpr int SN = 4 / SK;
+        constexpr int TPW = NTW * 4 / SN;   // 16-column tiles per wave
+        constexpr int U = TPW <= 4 ? 4 : 1; // chunks in flight per iteration
+        const int wk = w % SK, wn = w / SK;
         const int r = l & 15, kg = l >> 4;
         const int tA = min(t0 + r, T - 1);
         const uint16_t* xa = (const uint16_t*)p.x + (size_t)tA * H + kg * 16;
-        const uint16_t* wb[NTW];
-        f32x4_t acc[NTW];
+        const uint16_t* wb[TPW];
+        f32x4_t acc[TPW];
 #pragma unroll
-        for (int i = 0; i < NTW; ++i) {
-            const int col = min((w * NTW + i) * 16 + r, E - 1);
+        for (int i = 0; i < TPW; ++i) {
+            const int col = min((wn * TPW + i) * 16 + r, E - 1);
             wb[i] = (const uint16_t*)p.Wg + (size_t)col * H + kg * 16;
             acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
         }
-        for (int k0 = 0; k0 < H; k0 += 64) {
-            const bf16x8_t a0 = *(const bf16x8_t*)(xa + k0);
-            const bf16x8_t a1 = *(const bf16x8_t*)(xa + k0 + 8);
+        const int nch = H / 64;
+        for (int c = wk; c < nch; c += U * SK) {
+            bf16x8_t a[U][2], b[U][TPW][2];
 #pragma unroll
-            for (int i = 0; i < NTW; ++i) {
-                const bf16x8_t b0 = *(const bf16x8_t*)(wb[i] + k0);
-                const bf16x8_t b1 = *(const bf16x8_t*)(wb[i] + k0 + 8);
-                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b0, acc[i], 0, 0, 0);
-                acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b1, acc[i], 0, 0, 0);
+            for (int u = 0; u < U; ++u) {
+                const int k0 = min(c + u * SK, nch - 1) * 64;
+                a[u][0] = *(const bf16x8_t*)(xa + k0);
+                a[u][1] = *(const bf16x8_t*)(xa + k0 + 8);
+#pragma unroll
+                for (int i = 0; i < TPW; ++i) {
+                    b[u][i][0] = *(const bf16x8_t*)(wb[i] + k0);
+                    b[u][i][1] = *(const bf16x8_t*)(wb[i] + k0 + 8);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (c + u * SK < nch) {
+#pragma unroll
+                    for (int i = 0; i < TPW; ++i) {
+                        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][0], b[u][i][0], acc[i], 0, 0, 0);
+                        acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[u][1], b[u][i][1], acc[i], 0, 0, 0);
+                    }
+                }
             }
         }
         // D layout: lane l holds column (l & 15), rows 4*(l >> 4) + v
+        if constexpr (SK == 1) {
 #pragma unroll
-        for (int i = 0; i < NTW; ++i)
+            for (int i = 0; i < TPW; ++i)
 #pragma unroll
-            for (int v = 0; v < 4; ++v) s_log[kg * 4 + v][(w * NTW + i) * 16 + r] = acc[i][v];
+                for (int v = 0; v < 4; ++v) s_log[kg * 4 + v][(wn * TPW + i) * 16 + r] = acc[i][v];
+        } else {
+#pragma unroll
+            for (int i = 0; i < TPW; ++i)
+#pragma unroll
+                for (int v = 0; v < 4; ++v)
+                    s_part[wk][kg * 4 + v][(wn * TPW + i) * 16 + r] = acc[i][v];
+            __syncthreads();
+            for (int idx = tid; idx < kBM * EP; idx += kThreads) {
+                const int row = idx / EP, col = idx % EP;
+                float sum = s_part[0][row][col];
+#pragma unroll
+                for (int q = 1; q < SK; ++q) sum += s_part[q][row][col];
+                s_log[row][col] = sum;
+            }
+        }
     } else {
         const float* x = (const float*)p.x;
         const float* Wg = (const float*)p.Wg;
@@ -149,9 +213,11 @@ __global__ __launch_bounds__(kThreads) void k_route(RouteParams p)
     __syncthreads();
 
     // ---------------- synthetic affinity bias ----------------
-    if (p.pref != nullptr && p.aff_bias != 0.0f && p.n_pref > 0) {
-        const int np = p.n_pref;
-        for (int idx = tid; idx < kBM * np; idx += kThreads) {
+    if (do_bias) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (pre_o[q] >= 0 && pre_o[q] < E) s_log[pre_row[q]][s_o2s[pre_o[q]]] += p.aff_bias;
+        for (int idx = tid + 4 * kThreads; idx < kBM * np; idx += kThreads) {
             const int row = idx / np, j = idx % np;
             const int t = t0 + row;
             if (t < T) {
@@ -177,7 +243,8 @@ __global__ __launch_bounds__(kThreads) void k_route(RouteParams p)
         const int row = w + 4 * it;
         const int t = t0 + row;
         const bool active = t < T;  // wave-uniform
-        const int kt = !active ? 0 : (p.ragged ? clampi(p.k_tok[t], 0, p.k_max) : p.k_max);
+        const int kt = s_kt[row];
+        (void)active;
 
         float lg[NTW], key[NTW];
         uint32_t oid[NTW];
@@ -248,13 +315,7 @@ __global__ __launch_bounds__(kThreads) void k_route(RouteParams p)
 #pragma unroll
             for (int i = 0; i < NTW; ++i)
                 if (ok[i] && !taken[i]) better_take(buk, bid, bs, ordered_key(key[i]), oid[i], l + 64 * i);
-#pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) {
-                const uint32_t ouk = __shfl_xor(buk, o);
-                const uint32_t oi = __shfl_xor(bid, o);
-                const uint32_t os = __shfl_xor(bs, o);
-                better_take(buk, bid, bs, ouk, oi, os);
-            }
+            wave_argbest(buk, bid, bs);
 #pragma unroll
             for (int i = 0; i < NTW; ++i)
                 if (bs == (uint32_t)(l + 64 * i)) taken[i] = true;
@@ -262,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void k_route(RouteParams p)
         }
         if (kt == 0) continue;
 
-        const int base = p.row_ptr[t];
+        const int base = s_rp[row];
         const float mylog = s_log[row][l < kt ? myslot : 0];
         float wt;
         if (!sigm) {

@@ -62,25 +62,37 @@ __global__ __launch_bounds__(kThreads) void k_hist(ShParams p)
     if (threadIdx.x < p.P) p.o.thist[threadIdx.x * p.nb + b] = tcnt[threadIdx.x];
 }
 
-// In-place exclusive scan of n ints (one block of 1024 threads); returns total.
+// In-place exclusive scan of n ints (one block of 1024 threads); returns
+// the total.  16 consecutive entries per thread per pass, all loaded before
+// they are summed, so a pass costs about one memory latency.
 MOE_DEV int block_scan_inplace(int32_t* a, int n, int* smem)
 {
+    constexpr int kItems = 16;
     int carry = 0;
-    for (int base = 0; base < n; base += 4 * 1024) {
-        int v[4];
+    for (int base = 0; base < n; base += kItems * 1024) {
+        const int i0 = base + threadIdx.x * kItems;
+        int v[kItems];
+        if (i0 + kItems <= n) {
+#pragma unroll
+            for (int q = 0; q < kItems; q += 4) {
+                const int4 t = *(const int4*)(a + i0 + q);
+                v[q] = t.x;
+                v[q + 1] = t.y;
+                v[q + 2] = t.z;
+                v[q + 3] = t.w;
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < kItems; ++q) v[q] = i0 + q < n ? a[i0 + q] : 0;
+        }
         int sum = 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int i = base + threadIdx.x * 4 + q;
-            v[q] = i < n ? a[i] : 0;
-            sum += v[q];
-        }
+        for (int q = 0; q < kItems; ++q) sum += v[q];
         int total;
         int run = carry + block_excl_scan(sum, smem, &total);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int i = base + threadIdx.x * 4 + q;
-            if (i < n) a[i] = run;
+        for (int q = 0; q < kItems; ++q) {
+            if (i0 + q < n) a[i0 + q] = run;
             run += v[q];
         }
         carry += total;
