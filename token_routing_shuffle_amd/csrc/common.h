@@ -163,6 +163,16 @@ MOE_DEV int block_excl_scan(int v, int* smem, int* total)
     return r;
 }
 
+// Workgroup barrier that waits only for this wave's LDS operations.
+// __syncthreads() also fences global memory, which makes every barrier wait
+// for all outstanding global loads (vmcnt(0)) and so defeats prefetching
+// across barriers; LDS data written before this barrier is visible after it.
+MOE_DEV void lds_barrier()
+{
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt, expcnt untouched
+    __builtin_amdgcn_s_barrier();
+}
+
 MOE_DEV int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
 // Own fp32 exp: Cody-Waite additive range reduction n = rint(x*log2 e),

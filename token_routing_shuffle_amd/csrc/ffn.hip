@@ -26,13 +26,11 @@
 namespace moe {
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64;
+constexpr int BM = 128, BK = 64;
 constexpr int LDSK = BK;   // no padding: XOR-swizzled chunks
-constexpr int kThreads = 256;
 constexpr int kMaxSeg = 516;
 
 struct GemmParams {
-    int up;           // 1: GEMM1 + SwiGLU epilogue, 0: GEMM2
     int n_routed, e_begin, has_shared, T;
     const int32_t* expert_off;
     // routed operands
@@ -47,33 +45,112 @@ struct GemmParams {
     const uint16_t* shB;     // up: Wsh13 [2*Ish, H]; down: Wsh2 [H, Ish]
     uint16_t* shC;           // up: h_sh [T, Ish]; down: y_sh [T, H]
     int shK, shN;
+    int A_max;               // rows of the sorted row space (bounds of A, C)
 };
 
 MOE_DEV float silu(float g) { return g / (1.0f + expf(-g)); }
 
-template <bool UP>
-__global__ __launch_bounds__(kThreads, 2) void k_grouped_gemm(GemmParams p)
+// SiLU for the bf16 path, whose result is rounded to bf16 right after:
+// hardware exp2 and reciprocal (about 1 ulp each) are far inside that rounding.
+MOE_DEV float silu_fast(float g)
 {
-    // LDS: two stages of [A tile | B tile] (XOR-swizzled 128-byte rows);
-    // reused after the K loop to stage the output tile for 16-byte stores.
-    constexpr int kStage = (BM + BN) * LDSK;
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * kStage];
+    return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// Two floats -> packed bf16 pair (v_cvt_pk_bf16_f32, round to nearest even).
+MOE_DEV uint32_t pack2_bf16(float lo, float hi)
+{
+    const f32x2_t f = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
+}
+
+#define MOE_LDS_PTR(p) ((void __attribute__((address_space(3)))*)(p))
+
+// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left alone)
+template <int N>
+MOE_DEV void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// LDS fragment read issued as inline asm: the compiler's wait-count pass then
+// does not treat it as a read of the in-flight LDS DMA (it would drain all
+// outstanding loads before it); completion is waited for explicitly with
+// frag_wait, whose operands tie the fragments so no use moves above it.
+// (The asm exists only in the device pass; the host pass never runs these.)
+MOE_DEV bf16x8_t lds_read_b128(const uint16_t* p)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint32_t a = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const uint16_t*)p);
+    bf16x8_t v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(a));
+    return v;
+#else
+    return *(const bf16x8_t*)p;
+#endif
+}
+
+MOE_DEV void frag_wait(bf16x8_t (&a)[4], bf16x8_t (&b)[4])
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]),
+                   "+v"(b[2]), "+v"(b[3]));
+#else
+    (void)a;
+    (void)b;
+#endif
+}
+
+// Tile BM x BN x BK, BN/32 waves in a 2 x (BN/64) grid, each wave owning a
+// 64 x 64 block of the output (4 x 4 MFMA 16x16x32 tiles).  For the up
+// projection the BN columns are BN/2 gate neurons followed by the same BN/2
+// up neurons, and every wave holds matching gate and up columns so the SwiGLU
+// product is formed in registers.
+//
+// Operands go HBM/L2 -> LDS directly (buffer_load_dwordx4 ... lds): no
+// staging registers and no ds_write instructions.  LDS holds a ring of three
+// stages of [A tile | B tile]; rows are 128 bytes (eight 16-byte chunks),
+// XOR-swizzled (chunk c of row r at position c ^ (r & 7)), which keeps the
+// MFMA fragment reads free of bank conflicts; the swizzle is applied on the
+// global side, since each wave-wide LDS DMA writes 64 consecutive 16-byte
+// slots.  Each k-step: wait for this wave's DMA of tile kt, barrier, issue
+// the DMA of tile kt+2 into the stage read at step kt-1, compute tile kt.
+template <bool UP, int BN>
+__global__ __launch_bounds__(BN * 2, 1) void k_grouped_gemm(GemmParams p)
+{
+    constexpr int kThreads = BN * 2;        // BN/32 waves
+    constexpr int NW = kThreads / 64;
+    constexpr int WN = BN / 64;             // waves along N
+    constexpr int NPT = BN / 2;             // up: neurons per tile
+    constexpr int kRows = BM + BN;          // 128-byte rows per stage
+    constexpr int kStageE = kRows * 64;     // bf16 elements per stage
+    constexpr int NS = 3;                   // LDS stages
+    constexpr int NI = kRows * 8 / 64 / NW; // DMA instructions per wave per stage
+    static_assert(kRows * 8 == NI * 64 * NW, "stage split");
+    static_assert(BM % 8 == 0, "a DMA instruction covers 8 rows of one operand");
+    __shared__ __attribute__((aligned(16))) uint16_t smem[NS * kStageE];
     __shared__ int s_pref[kMaxSeg + 1];
     __shared__ int s_row0[kMaxSeg];
     __shared__ int s_cnt[kMaxSeg];
     __shared__ int s_smem[17];
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6, l = tid & 63;
-    const int wm = w >> 1, wn = w & 1;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
+    const int wm = w / WN, wn = w % WN;
     const int nseg = p.n_routed + p.has_shared;
 
-    // ---- tile list prefix over segments (3 segments per thread at most)
+    // ---- tile list prefix over segments
     {
-        int tiles[3], sum = 0;
+        constexpr int SPT = (kMaxSeg + kThreads - 1) / kThreads;
+        int tiles[SPT], sum = 0;
 #pragma unroll
-        for (int q = 0; q < 3; ++q) {
-            const int i = tid * 3 + q;
+        for (int q = 0; q < SPT; ++q) {
+            const int i = tid * SPT + q;
             tiles[q] = 0;
             if (i < nseg) {
                 int row0, cnt, nt;
@@ -81,11 +158,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_gemm(GemmParams p)
                     const int e = p.e_begin + i;
                     row0 = p.expert_off[e];
                     cnt = p.expert_off[e + 1] - row0;
-                    nt = UP ? p.N / 64 : p.N / BN;
+                    nt = UP ? p.N / NPT : p.N / BN;
                 } else {
                     row0 = 0;
                     cnt = p.T;
-                    nt = UP ? p.shN / 64 : p.shN / BN;
+                    nt = UP ? p.shN / NPT : p.shN / BN;
                 }
                 s_row0[i] = row0;
                 s_cnt[i] = cnt;
@@ -96,8 +173,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_gemm(GemmParams p)
         int total;
         int run = block_excl_scan(sum, s_smem, &total);
 #pragma unroll
-        for (int q = 0; q < 3; ++q) {
-            const int i = tid * 3 + q;
+        for (int q = 0; q < SPT; ++q) {
+            const int i = tid * SPT + q;
             if (i < nseg) s_pref[i] = run;
             run += tiles[q];
         }
@@ -109,9 +186,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_gemm(GemmParams p)
     const int L0 = (int)(((long long)total * xcd) >> 3);
     const int L1 = (int)(((long long)total * (xcd + 1)) >> 3);
 
-    const int lr = tid >> 3;        // loader row 0..31 (+32 q)
-    const int lc = (tid & 7) * 8;   // loader k offset (elements)
-
     for (int L = L0 + j; L < L1; L += G8) {
         // ---- locate the tile
         int lo = 0, hi = nseg - 1;
@@ -119,41 +193,77 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_gemm(GemmParams p)
             const int mid = (lo + hi + 1) >> 1;
             if (s_pref[mid] <= L) lo = mid; else hi = mid - 1;
         }
-        const int seg = lo;
+        // tile values are wave-uniform: keep them in scalar registers
+        const int seg = __builtin_amdgcn_readfirstlane(lo);
         const bool shared = seg >= p.n_routed;
-        const int row0 = s_row0[seg], cnt = s_cnt[seg];
+        const int row0 = __builtin_amdgcn_readfirstlane(s_row0[seg]);
+        const int cnt = __builtin_amdgcn_readfirstlane(s_cnt[seg]);
         const int mt = (cnt + BM - 1) / BM;
-        const int local = L - s_pref[seg];
+        const int local = L - __builtin_amdgcn_readfirstlane(s_pref[seg]);
         const int ntile = local / mt, m0 = (local % mt) * BM;
         const int K = shared ? p.shK : p.K;
         const int N = shared ? p.shN : p.N;
         const int rows = min(BM, cnt - m0);
 
-        // ---- operand row pointers (rows past the segment end repeat its last row)
-        const uint16_t* ap[4];
-        const uint16_t* bp[4];
-        const uint16_t* Bseg = shared ? p.shB : p.B + (size_t)(p.e_begin + seg) * (UP ? 2 * (size_t)N : (size_t)N) * K;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int r = lr + 32 * q;
-            const int gr = row0 + m0 + min(r, rows - 1);
-            const uint16_t* arow;
-            if (shared)
-                arow = p.shA + (size_t)gr * K;
-            else if (p.A != nullptr)
-                arow = p.A + (size_t)gr * K;
-            else
-                arow = p.X + (size_t)p.row_tok[gr] * K;
-            ap[q] = arow + lc;
-            int brow;
-            if (UP) {
-                const int n0 = ntile * 64;
-                brow = r < 64 ? n0 + r : N + n0 + (r - 64);
-            } else {
-                brow = ntile * BN + r;
-            }
-            bp[q] = Bseg + (size_t)brow * K + lc;
+        // ---- operands as buffer resources (base + bounds); per-lane 32-bit
+        // row offsets; the k-step goes in the scalar offset.  Rows past the
+        // segment end repeat its last row.
+        const uint16_t* Abase;
+        int a_bytes;
+        if (shared) {
+            Abase = p.shA;
+            a_bytes = p.T * K * 2;
+        } else if (p.A != nullptr) {
+            Abase = p.A;
+            a_bytes = p.A_max * K * 2;
+        } else {
+            Abase = p.X;
+            a_bytes = p.T * K * 2;
         }
+        const uint16_t* Bseg = shared ? p.shB : p.B + (size_t)(p.e_begin + seg) * (UP ? 2 * (size_t)N : (size_t)N) * K;
+        const int b_bytes = (UP ? 2 * N : N) * K * 2;
+        const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc((void*)Abase, (short)0, a_bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc((void*)Bseg, (short)0, b_bytes, 0x00020000);
+        // DMA instruction jj of this wave covers stage rows [8(w*NI+jj), +8);
+        // lane l fills slot l: row 8(w*NI+jj) + l/8, position l%8, which holds
+        // the row's global chunk (l%8) ^ (row & 7).
+        int doff[NI];
+#pragma unroll
+        for (int jj = 0; jj < NI; ++jj) {
+            const int row = (w * NI + jj) * 8 + (l >> 3);
+            const int chunk = (l & 7) ^ (row & 7);
+            if (row < BM) {
+                const int gr = row0 + m0 + min(row, rows - 1);
+                const int src_row = (!shared && p.A == nullptr) ? p.row_tok[gr] : gr;
+                doff[jj] = src_row * K * 2 + chunk * 16;
+            } else {
+                const int r = row - BM;
+                int brow;
+                if (UP) {
+                    const int n0 = ntile * NPT;
+                    brow = r < NPT ? n0 + r : N + n0 + (r - NPT);
+                } else {
+                    brow = ntile * BN + r;
+                }
+                doff[jj] = brow * K * 2 + chunk * 16;
+            }
+        }
+        auto dma = [&](int kt, int st) {
+            const int ko = kt * BK * 2;
+#pragma unroll
+            for (int jj = 0; jj < NI; ++jj) {
+                uint16_t* dst = smem + st * kStageE + (w * NI + jj) * 512;
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass cannot form LDS pointers
+                if ((w * NI + jj) * 8 < BM)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, MOE_LDS_PTR(dst), 16, doff[jj], ko, 0, 0);
+                else
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, MOE_LDS_PTR(dst), 16, doff[jj], ko, 0, 0);
+#else
+                (void)dst;
+                (void)ko;
+#endif
+            }
+        };
 
         f32x4_t acc[4][4];
 #pragma unroll
@@ -161,106 +271,90 @@ __global__ __launch_bounds__(kThreads, 2) void k_grouped_gemm(GemmParams p)
 #pragma unroll
             for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-        // global -> register stages, two k-tiles ahead of the MFMAs
-        u32x4_t r0a[4], r0b[4], r1a[4], r1b[4];
-        auto gload = [&](u32x4_t* ra, u32x4_t* rb, int kt) {
-            const int ko = kt * BK;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                ra[q] = *(const u32x4_t*)(ap[q] + ko);
-                rb[q] = *(const u32x4_t*)(bp[q] + ko);
-            }
-        };
-        auto lstore = [&](const u32x4_t* ra, const u32x4_t* rb, int buf) {
-            uint16_t* As = smem + buf * kStage;
-            uint16_t* Bs = As + BM * LDSK;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int row = lr + 32 * q;
-                const int pos = (((lc >> 3) ^ (row & 7)) << 3);
-                *(u32x4_t*)&As[row * LDSK + pos] = ra[q];
-                *(u32x4_t*)&Bs[row * LDSK + pos] = rb[q];
-            }
-        };
-        auto compute = [&](int buf) {
-            const uint16_t* As = smem + buf * kStage;
-            const uint16_t* Bs = As + BM * LDSK;
-#pragma unroll
-            for (int kk = 0; kk < BK; kk += 32) {
-                bf16x8_t af[4], bfr[4];
+        auto compute = [&](int st) {
+            const uint16_t* As = smem + st * kStageE;
+            const uint16_t* Bs = As + BM * BK;
+            bf16x8_t af[2][4], bfr[2][4];
+            auto read = [&](int kk) {
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt) {
                     const int row = wm * 64 + rt * 16 + (l & 15);
-                    const int pos = ((((kk >> 3) + (l >> 4)) ^ (row & 7)) << 3);
-                    af[rt] = *(const bf16x8_t*)&As[row * LDSK + pos];
+                    af[kk][rt] = lds_read_b128(&As[row * BK + ((((kk << 2) + (l >> 4)) ^ (row & 7)) << 3)]);
                 }
 #pragma unroll
                 for (int ct = 0; ct < 4; ++ct) {
-                    const int cb = UP ? ((ct < 2) ? wn * 32 + ct * 16 : 64 + wn * 32 + (ct - 2) * 16)
+                    const int cb = UP ? ((ct < 2) ? wn * 32 + ct * 16 : NPT + wn * 32 + (ct - 2) * 16)
                                       : wn * 64 + ct * 16;
                     const int row = cb + (l & 15);
-                    const int pos = ((((kk >> 3) + (l >> 4)) ^ (row & 7)) << 3);
-                    bfr[ct] = *(const bf16x8_t*)&Bs[row * LDSK + pos];
+                    bfr[kk][ct] = lds_read_b128(&Bs[row * BK + ((((kk << 2) + (l >> 4)) ^ (row & 7)) << 3)]);
                 }
+            };
+            auto mfma = [&](int kk) {
 #pragma unroll
                 for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
                     for (int ct = 0; ct < 4; ++ct)
-                        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[rt], bfr[ct], acc[rt][ct], 0, 0, 0);
-            }
+                        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[kk][ct], af[kk][rt], acc[rt][ct], 0, 0, 0);
+            };
+            read(0);
+            frag_wait(af[0], bfr[0]);
+            read(1);             // overlaps the first half's MFMAs
+            mfma(0);
+            frag_wait(af[1], bfr[1]);
+            mfma(1);
         };
 
         const int KT = K / BK;
-        gload(r0a, r0b, 0);
-        lstore(r0a, r0b, 0);
-        if (KT > 1) gload(r1a, r1b, 1);
-        if (KT > 2) gload(r0a, r0b, 2);
-        __syncthreads();
-        // invariant at even kt: LDS buf 0 holds tile kt, r1 holds kt+1, r0 holds kt+2
-        for (int kt = 0; kt < KT; kt += 2) {
-            compute(0);
-            if (kt + 1 < KT) lstore(r1a, r1b, 1);
-            if (kt + 3 < KT) gload(r1a, r1b, kt + 3);
-            __syncthreads();
-            if (kt + 1 < KT) {
-                compute(1);
-                if (kt + 2 < KT) lstore(r0a, r0b, 0);
-                if (kt + 4 < KT) gload(r0a, r0b, kt + 4);
-                __syncthreads();
-            }
+        dma(0, 0);
+        if (KT > 1) dma(1, 1);
+        int st = 0;
+        for (int kt = 0; kt < KT; ++kt) {
+            // this wave's DMA of tile kt is done once at most the NI loads of
+            // tile kt+1 are still outstanding
+            if (kt + 1 < KT) wait_vmcnt<NI>(); else wait_vmcnt<0>();
+            __builtin_amdgcn_s_barrier();
+            if (kt + 2 < KT) dma(kt + 2, st == 0 ? 2 : st - 1);
+            compute(st);
+            st = st == 2 ? 0 : st + 1;
         }
+        __syncthreads();
 
-        // ---- epilogue: D lane layout: column (l & 15), rows 4*(l >> 4) + v.
-        // Stage the bf16 tile in LDS, then write 16-byte row chunks.
+        // ---- epilogue.  The MFMAs compute the transposed tile (B rows as
+        // the first operand), so lane l holds output row (l & 15) and four
+        // consecutive output columns 4*(l >> 4) + v: packed into one 8-byte
+        // LDS store, then written out as 16-byte row chunks.
         uint16_t* Cseg = shared ? p.shC : p.C;
-        constexpr int CW = UP ? 64 : BN;   // output columns of the tile
+        constexpr int CW = UP ? NPT : BN;  // output columns of the tile
         constexpr int CS = CW + 8;         // padded LDS row stride
         uint16_t* Cs = smem;
         if (UP) {
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-                for (int c = 0; c < 2; ++c)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int row = wm * 64 + rt * 16 + (l >> 4) * 4 + v;
-                        const float g = acc[rt][c][v], u = acc[rt][c + 2][v];
-                        Cs[row * CS + wn * 32 + c * 16 + (l & 15)] = (uint16_t)f2bf(silu(g) * u);
-                    }
+                for (int c = 0; c < 2; ++c) {
+                    const int row = wm * 64 + rt * 16 + (l & 15);
+                    const f32x4_t g = acc[rt][c], u = acc[rt][c + 2];
+                    uint2 v;
+                    v.x = pack2_bf16(silu_fast(g[0]) * u[0], silu_fast(g[1]) * u[1]);
+                    v.y = pack2_bf16(silu_fast(g[2]) * u[2], silu_fast(g[3]) * u[3]);
+                    *(uint2*)&Cs[row * CS + wn * 32 + c * 16 + (l >> 4) * 4] = v;
+                }
         } else {
 #pragma unroll
             for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-                for (int ct = 0; ct < 4; ++ct)
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int row = wm * 64 + rt * 16 + (l >> 4) * 4 + v;
-                        Cs[row * CS + wn * 64 + ct * 16 + (l & 15)] = (uint16_t)f2bf(acc[rt][ct][v]);
-                    }
+                for (int ct = 0; ct < 4; ++ct) {
+                    const int row = wm * 64 + rt * 16 + (l & 15);
+                    const f32x4_t a = acc[rt][ct];
+                    uint2 v;
+                    v.x = pack2_bf16(a[0], a[1]);
+                    v.y = pack2_bf16(a[2], a[3]);
+                    *(uint2*)&Cs[row * CS + wn * 64 + ct * 16 + (l >> 4) * 4] = v;
+                }
         }
         __syncthreads();
         constexpr int CPR = CW / 8;        // 16-byte chunks per row
-        const int n_out = UP ? ntile * 64 : ntile * BN;
+        const int n_out = UP ? ntile * NPT : ntile * BN;
 #pragma unroll
         for (int q = 0; q < (BM * CPR) / kThreads; ++q) {
             const int idx = tid + q * kThreads;
@@ -336,14 +430,24 @@ int num_cus()
     return cached[dev];
 }
 
+template <bool UP, int BN>
+hipError_t launch_gemm_t(const GemmParams& p, long long ub, hipStream_t s)
+{
+    // one resident block per CU (three LDS stages: 96 or 144 KB)
+    long long grid = std::min<long long>(ub, (long long)num_cus());
+    grid = (grid + 7) / 8 * 8;
+    hipLaunchKernelGGL((k_grouped_gemm<UP, BN>), dim3((unsigned)grid), dim3(BN * 2), 0, s, p);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm(const moe_cfg& c, const FfnArgs& a, bool up, hipStream_t s)
 {
     GemmParams p;
-    p.up = up;
     p.n_routed = a.n_routed;
     p.e_begin = a.e_begin;
     p.has_shared = a.sh_x != nullptr;
     p.T = c.T;
+    p.A_max = a.A_max;
     p.expert_off = a.expert_off;
     if (up) {
         p.A = (const uint16_t*)a.xs;
@@ -372,24 +476,19 @@ hipError_t launch_gemm(const moe_cfg& c, const FfnArgs& a, bool up, hipStream_t 
         p.shK = a.Ish;
         p.shN = c.H;
     }
+    // wide tiles (BN = 256) when every segment's N splits into them
+    const int nw_r = up ? 2 * c.I : c.H;
+    const int nw_s = up ? 2 * a.Ish : c.H;
+    const bool wide = (a.n_routed == 0 || nw_r % 256 == 0) && (!p.has_shared || nw_s % 256 == 0);
+    const int BN = wide ? 256 : 128;
     // host upper bound on the tile count (A is only known on the device)
     long long ub = 0;
-    if (a.n_routed > 0) {
-        const int nt = up ? c.I / 64 : c.H / BN;
-        ub += ((long long)ceil_div(a.A_max, BM) + a.n_routed) * nt;
-    }
-    if (p.has_shared) {
-        const int nt = up ? a.Ish / 64 : c.H / BN;
-        ub += (long long)ceil_div(c.T, BM) * nt;
-    }
+    if (a.n_routed > 0) ub += ((long long)ceil_div(a.A_max, BM) + a.n_routed) * (nw_r / BN);
+    if (p.has_shared) ub += (long long)ceil_div(c.T, BM) * (nw_s / BN);
     if (ub == 0) return hipSuccess;
-    long long grid = std::min<long long>(ub, 2LL * num_cus());
-    grid = (grid + 7) / 8 * 8;
     if (up)
-        hipLaunchKernelGGL(k_grouped_gemm<true>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
-    else
-        hipLaunchKernelGGL(k_grouped_gemm<false>, dim3((unsigned)grid), dim3(kThreads), 0, s, p);
-    return hipGetLastError();
+        return wide ? launch_gemm_t<true, 256>(p, ub, s) : launch_gemm_t<true, 128>(p, ub, s);
+    return wide ? launch_gemm_t<false, 256>(p, ub, s) : launch_gemm_t<false, 128>(p, ub, s);
 }
 
 hipError_t launch_f32(const moe_cfg& c, const FfnArgs& a, bool up, hipStream_t s)
