@@ -162,7 +162,9 @@ def route(l, cfg, k_tok=None, ebias=None):
         valid = sel >= 0
         ps = np.where(valid, np.take_along_axis(p, np.maximum(sel, 0), axis=1), 0.0)
         if cfg.renorm:
-            w = ps / ps.sum(axis=1, keepdims=True)
+            # a token with routing budget k_t = 0 selects nothing: no weights
+            tot = ps.sum(axis=1, keepdims=True)
+            w = np.divide(ps, tot, out=np.zeros_like(ps), where=tot > 0)
         else:
             w = ps
     elif cfg.gate == "sigmoid_grouped":
@@ -171,7 +173,8 @@ def route(l, cfg, k_tok=None, ebias=None):
         s64 = 1.0 / (1.0 + np.exp(-l64))
         valid = sel >= 0
         ss = np.where(valid, np.take_along_axis(s64, np.maximum(sel, 0), axis=1), 0.0)
-        w = cfg.route_scale * ss / ss.sum(axis=1, keepdims=True)
+        tot = ss.sum(axis=1, keepdims=True)
+        w = cfg.route_scale * np.divide(ss, tot, out=np.zeros_like(ss), where=tot > 0)
     else:
         raise ValueError(cfg.gate)
     return sel, w

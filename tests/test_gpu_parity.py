@@ -299,3 +299,102 @@ def test_relabelling_invariance(name, T):
     a = run_forward(c1, exports=False)["out"]
     b = run_forward(c0, exports=False)["out"]
     assert torch.equal(a, b)
+
+
+# ---------------------------------------------------------------- edge cases
+
+EDGE = {
+    # one token, k = E (every expert selected), P = 1 (one group: LAR = 1)
+    "tiny_T1_kE_P1": ("tiny", 1, dict(k=8, P=1)),
+    # P = E: every slot its own placement group
+    "tiny_PE": ("tiny", 64, dict(P=8)),
+    # bf16 layer smaller than one tile per expert, E not a multiple of 64
+    "bf16_small_E8": ("dsv2lite", 37, dict(E=8, k=3, n_pref=3, P=2)),
+    # every token the same ID: affinity sends all tokens to the same experts
+    # (a few large experts spanning several tiles, many empty experts)
+    "one_token_id": ("qwen3", 700, dict(zipf_s=60.0)),
+    # ragged k with many zero-k requests
+    "prism_ragged_zeros": ("prism", 640, dict(k_choices=(0, 0, 8, 32))),
+}
+
+
+@pytest.mark.parametrize("key", list(EDGE))
+def test_edge_forward(key):
+    name, T, over = EDGE[key]
+    c = hn.make_case(name, T, profile_tokens=1024, **over)
+    if key == "one_token_id":
+        assert len(np.unique(c.tok)) == 1
+    r = run_forward(c)
+    l64, sel_or, w_or, rp_or, slot_or, _ = oracle_routing(c)
+    E = c.cfg.E
+    np.testing.assert_array_equal(r["row_ptr"][:T + 1], rp_or)
+    A = int(rp_or[-1])
+    l_gpu = np.empty((T, E))
+    l_gpu[:, c.tables.slot_to_orig] = r["logits"][:T * E].reshape(T, E)
+    sel_gpu, _ = csr_to_sel(c, r["row_ptr"], r["topk_slot"][:A])
+    ndiff = hn.check_selection(c, sel_gpu, l64, l_gpu, k_tok_of(c))
+    same = (sel_gpu == sel_or).all(axis=1)
+    ref = mo.moe_output(c.h["x"], sel_or, w_or, c.h["W13"], c.h["W2"], c.cfg.I, c.h.get("Wsh13"),
+                        c.h.get("Wsh2"), c.cfg.n_shared, c.cfg.I_shared)
+    got = hn.f64_of(hn.host(r["out"]))
+    err = hn.rel_err(got[same], ref[same])
+    print("[edge] %s: T=%d A=%d rel err %.3g, %d near-tie tokens" % (key, T, A, err, ndiff))
+    assert err <= hn.tol_out(c.cfg)
+    if ndiff == 0:
+        ref_sh = mo.shuffle(rp_or, slot_or, c.tok, c.lut, E, c.cfg.P)
+        for n in ("expert_count", "expert_off", "group_off", "pair_count", "tok_perm", "tok_off"):
+            np.testing.assert_array_equal(r[n][:ref_sh[n].size], ref_sh[n].reshape(-1), err_msg=n)
+        np.testing.assert_array_equal(r["sorted_to_assign"][:A], ref_sh["sorted_to_assign"])
+        if c.cfg.P == 1:
+            assert ref_sh["lar"] == 1.0
+
+
+def test_empty_layer():
+    """T = 0: every call succeeds and writes only the empty offsets."""
+    m = moe_mod()
+    from token_routing_shuffle_amd import workload as wl
+    cfg = wl.CONFIGS["dsv2lite"].replace(T=0)
+    c = m.make_cfg(cfg)
+    ws = m.workspace(c)
+    E, P = cfg.E, cfg.P
+    ex = dict(row_ptr=hn.dev_i32(1), expert_count=hn.dev_i32(E), expert_off=hn.dev_i32(E + 1),
+              group_count=hn.dev_i32(P), group_off=hn.dev_i32(P + 1), pair_count=hn.dev_i32(P * P),
+              tok_off=hn.dev_i32(P + 1))
+    for v in ex.values():
+        v.fill_(-7)
+    d = {k: torch.zeros(8, dtype=torch.bfloat16, device=hn.DEV) for k in ("Wg", "W13", "W2", "Wsh13", "Wsh2")}
+    d["slot_to_orig"] = torch.arange(E, dtype=torch.int32, device=hn.DEV)
+    d["lut"] = torch.zeros(cfg.V, dtype=torch.int32, device=hn.DEV)
+    out = torch.empty((1, cfg.H), dtype=torch.bfloat16, device=hn.DEV)
+    x = torch.zeros((1, cfg.H), dtype=torch.bfloat16, device=hn.DEV)
+    tok = hn.dev_i32(1)
+    m.moe_forward(c, m.weights_struct(d), m.inputs_struct(x, tok), out, m.exports_struct(ex), ws)
+    torch.cuda.synchronize()
+    assert ex["row_ptr"][0].item() == 0
+    for n in ("expert_count", "expert_off", "group_count", "group_off", "pair_count", "tok_off"):
+        assert (ex[n] == 0).all(), n
+
+
+def test_ffn_group_share_matches_full():
+    """moe_expert_ffn over each placement group's slot range (one device's
+    share) reproduces the full call row for row."""
+    c = case("qwen3_1500")
+    m = moe_mod()
+    cfg = m.make_cfg(c.cfg)
+    E, P, H, A_max = c.cfg.E, c.cfg.P, c.cfg.H, c.cfg.T * c.cfg.k
+    _, _, _, rp, slot, _ = oracle_routing(c)
+    ref = mo.shuffle(rp, slot, c.tok, c.lut, E, P)
+    A = int(rp[-1])
+    xs = torch.zeros((A_max, H), dtype=torch.bfloat16, device=hn.DEV)
+    xs[:A] = hn.to_dev(mo.gather(c.h["x"], ref["sorted_to_assign"], rp))
+    off = hn.to_dev(ref["expert_off"])
+    ws = m.workspace(cfg)
+    full = torch.zeros_like(xs)
+    m.moe_expert_ffn(cfg, m.MOE_FFN_ROUTED, xs, None, None, None, off, c.dev["W13"], c.dev["W2"], 0, E, full, ws)
+    parts = torch.zeros_like(xs)
+    epg = E // P
+    for g in range(P):
+        m.moe_expert_ffn(cfg, m.MOE_FFN_ROUTED, xs, None, None, None, off, c.dev["W13"], c.dev["W2"],
+                         g * epg, (g + 1) * epg, parts, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(full[:A], parts[:A])

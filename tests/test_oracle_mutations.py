@@ -32,9 +32,12 @@ PY_MUTANTS = {
     "logits_operand_transposed": ("l = f64(x) @ f64(Wg).T", "l = (f64(Wg) @ f64(x).T).T[:, ::-1]"),
     "affinity_bias_wrong_rows": ("rows = np.repeat(np.arange(l.shape[0]), pref.shape[1])",
                                  "rows = np.tile(np.arange(l.shape[0]), pref.shape[1])"),
-    "renorm_dropped": ("            w = ps / ps.sum(axis=1, keepdims=True)", "            w = ps"),
-    "route_scale_dropped": ("w = cfg.route_scale * ss / ss.sum(axis=1, keepdims=True)",
-                            "w = ss / ss.sum(axis=1, keepdims=True)"),
+    "renorm_dropped": ("            w = np.divide(ps, tot, out=np.zeros_like(ps), where=tot > 0)",
+                       "            w = ps"),
+    "route_scale_dropped": ("w = cfg.route_scale * np.divide(ss, tot, out=np.zeros_like(ss), where=tot > 0)",
+                            "w = np.divide(ss, tot, out=np.zeros_like(ss), where=tot > 0)"),
+    "zero_budget_weights_nan": ("w = np.divide(ps, tot, out=np.zeros_like(ps), where=tot > 0)",
+                                "w = ps / tot"),
     "silu_sign": ("return g / (1.0 + np.exp(-g))", "return g / (1.0 + np.exp(g))"),
     "gate_up_swapped": ("return ffn(x64, w13[:I], w13[I:], W2[e])",
                         "return ffn(x64, w13[I:], w13[:I], W2[e])"),

@@ -167,6 +167,21 @@ def test_select_signed_zero_is_a_tie():
     assert mo.select(key, 2)[0].tolist() == [0, 1]
 
 
+def test_zero_budget_token_gets_no_routed_output():
+    # MoE-Prism treats k as a per-request knob; with k_t = 0 nothing is selected
+    rng = np.random.default_rng(4)
+    l = rng.standard_normal((3, 6))
+    k_tok = np.array([2, 0, 1], np.int32)
+    sel, w = mo.route(l, Cfg(k=2, renorm=True), k_tok)
+    assert (sel[1] == -1).all() and (w[1] == 0).all()
+    np.testing.assert_allclose(w[[0, 2]].sum(axis=1), 1.0)
+    W13 = rng.standard_normal((6, 8, 5))
+    W2 = rng.standard_normal((6, 5, 4))
+    x = rng.standard_normal((3, 5))
+    out = mo.moe_output(x, sel, w, W13, W2, 4)
+    assert np.isfinite(out).all() and (out[1] == 0).all()
+
+
 def test_select_ragged_k():
     rng = np.random.default_rng(3)
     key = rng.standard_normal((6, 10)).astype(np.float32)
