@@ -32,7 +32,8 @@ def parse():
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--fuse-gather", type=int, default=int(os.environ.get("MOE_BENCH_FUSE_GATHER", "1")))
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample", type=int, default=256, help="tokens in the oracle's timed sample")
+    ap.add_argument("--cpu-sample", type=int, default=4096,
+                    help="tokens in the oracle's timed sample (capped at the layer's T)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB "
                          "(reference point for HBM byte counters)")
@@ -119,34 +120,31 @@ def main():
         stage_ms[name] = float(np.mean(v))
 
     if args.copy_calib_mb > 0:
-        n = args.copy_calib_mb << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration(args.copy_calib_mb, torch, dev)
     A = int(row_ptr[T].item())
     pc = pair.cpu().numpy().reshape(P, P)
     counts = ecount.cpu().numpy()
     alg = algorithmic(cfg, A)
     up_ms = stage_ms["ffn_up"]
     achieved = alg["ffn_up_flops"] / (up_ms * 1e-3) / 1e12
+    traffic, traffic_note = measured_traffic(args.workload)
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
-                "traffic": None, "kernel": "k_grouped_gemm (GEMM1 + SwiGLU, routed + shared)",
+                "traffic": traffic, "traffic_unit": "bytes per launch", "traffic_source": traffic_note,
+                "kernel": "k_grouped_gemm<true,256> (GEMM1 + SwiGLU, routed + shared)",
                 "flops_per_launch": alg["ffn_up_flops"], "avg_launch_ms": round(up_ms, 4)}
     secondary = {
         "ffn_down_tflops": round(alg["ffn_down_flops"] / (stage_ms["ffn_down"] * 1e-3) / 1e12, 2),
         "combine_gbs": round(alg["combine_bytes"] / (stage_ms["combine"] * 1e-3) / 1e9, 1),
-        "dispatch_gbs": round(alg["dispatch_bytes"] / ((stage_ms["shuffle"] + stage_ms["gather"] +
-                                                        stage_ms["ffn_up"] * 0) * 1e-3) / 1e9, 1)
+        # with the gather fused into GEMM1 there is no separate dispatch copy to time
+        "dispatch_gbs": round(alg["dispatch_bytes"] /
+                              ((stage_ms["shuffle"] + stage_ms["gather"]) * 1e-3) / 1e9, 1)
         if args.fuse_gather == 0 else None,
     }
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, tables, w, x, np, torch, args.cpu_sample)
+        cpu = cpu_baseline(cfg, tables, w, x, np, torch, min(args.cpu_sample, cfg.T))
 
     res = {
         "metric": "MoE-layer tokens/s on 1 MI355X",
@@ -174,6 +172,52 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+def copy_calibration(mb, torch, dev):
+    """One plain streaming kernel of known size for scaling HBM byte
+    counters: bitwise_not over mb MiB of int32 (reads mb MiB, writes mb MiB).
+    The source is written first and then pushed out of the 256 MB Infinity
+    Cache by a 1 GiB fill, so the kernel's reads come from HBM."""
+    n = (mb << 20) // 4
+    src = torch.empty(n, dtype=torch.int32, device=dev).fill_(1)
+    evict = torch.empty(1 << 28, dtype=torch.int32, device=dev).fill_(2)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst, evict
+
+
+def _gemm_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("ffn.hip", "common.h", "internal.h"):
+        with open(os.path.join(ROOT, "token_routing_shuffle_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the GEMM1 kernel, from the committed summary of
+    the rocprofv3 FETCH_SIZE / WRITE_SIZE passes (already scaled by the copy
+    calibration).  None when there is no summary for this workload or when
+    the kernel sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "ffn_up_gemm_%s_pmc.md" % workload)
+    if not os.path.exists(path):
+        return None, "no counter summary for this workload"
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and line.startswith("- `"):
+                k, _, v = line[3:].partition("`:")
+                kv[k.strip()] = v.strip()
+    try:
+        if kv.get("source_sha256") != _gemm_source_hash():
+            return None, "kernel changed since the counters were taken"
+        return float(kv["traffic_bytes_per_launch"]), os.path.relpath(path, ROOT)
+    except (KeyError, ValueError):
+        return None, "counter summary unreadable"
 
 
 def cpu_baseline(cfg, tables, w, x, np, torch, n_sample):
@@ -214,8 +258,8 @@ def cpu_baseline(cfg, tables, w, x, np, torch, n_sample):
     return {"value": round(n_sample / dt, 2), "unit": "tokens/s", "cores": threads,
             "kind": "oracle", "wall_s": round(dt, 2),
             "sample": "first %d of %d tokens of the same layer (fp64 numpy oracle: logits, "
-                      "routing, dispatch metadata, dense per-token MoE incl. shared experts)"
-                      % (n_sample, cfg.T)}
+                      "routing, dispatch metadata with a v mod P lookup table, dense per-token "
+                      "MoE incl. shared experts)" % (n_sample, cfg.T)}
 
 
 if __name__ == "__main__":

@@ -110,12 +110,16 @@ typedef struct moe_cfg {
 } moe_cfg;
 
 /*
- * Host only; needs no GPU.  Checks the description: positive T, H, E, P, I,
- * V; k_max in [1, min(E, 64)]; E % P == 0 and E/P a power of two; E*P <= 4096;
- * E <= 512; n_pref in [0, E]; for bf16 H % 128 == 0, I % 64 == 0 and
- * (n_shared*I_shared) % 64 == 0; sigmoid gate only with n_rgroups dividing E,
- * 1 <= topk_rgroups <= n_rgroups, 1 <= rgroup_topn <= E/n_rgroups, and at
- * least k_max experts in the kept groups.  Returns MOE_OK or the error code.
+ * Host only; needs no GPU.  Checks the description: T >= 0 (an empty layer
+ * is valid: the calls then enqueue nothing that reads a row); positive H, E,
+ * P, I, V; k_max in [1, min(E, 64)]; T * k_max < 2^31 and T * k_max * H
+ * < 2^40; E <= 512; E % P == 0 and E/P a power of two; P <= 64 and
+ * E*P <= 4096; n_pref in [0, E]; H % 8 == 0; for bf16 H % 128 == 0,
+ * I % 64 == 0 and (n_shared*I_shared) % 64 == 0; sigmoid gate only with
+ * n_rgroups in [1, 64] dividing E, 1 <= topk_rgroups <= n_rgroups,
+ * 1 <= rgroup_topn <= min(8, E/n_rgroups), at least k_max experts in the
+ * kept groups and a finite route_scale; aff_bias not NaN.  Returns MOE_OK
+ * or the error code (MOE_ESHAPE, MOE_EDTYPE, MOE_EINVAL).
  */
 int32_t moe_validate(const moe_cfg* cfg);
 
