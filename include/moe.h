@@ -113,7 +113,9 @@ typedef struct moe_cfg {
  * Host only; needs no GPU.  Checks the description: T >= 0 (an empty layer
  * is valid: the calls then enqueue nothing that reads a row); positive H, E,
  * P, I, V; k_max in [1, min(E, 64)]; T * k_max < 2^31 and T * k_max * H
- * < 2^40; E <= 512; E % P == 0 and E/P a power of two; P <= 64 and
+ * < 2^40; for bf16 also T * k_max * max(H, I) * 2 and
+ * T * max(H, n_shared*I_shared) * 2 below 2^31 bytes (32-bit row offsets in
+ * the grouped GEMMs); E <= 512; E % P == 0 and E/P a power of two; P <= 64 and
  * E*P <= 4096; n_pref in [0, E]; H % 8 == 0; for bf16 H % 128 == 0,
  * I % 64 == 0 and (n_shared*I_shared) % 64 == 0; sigmoid gate only with
  * n_rgroups in [1, 64] dividing E, 1 <= topk_rgroups <= n_rgroups,

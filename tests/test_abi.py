@@ -76,6 +76,7 @@ def test_every_workload_config_validates(m):
     ("n_pref", 65, "MOE_ESHAPE"),
     ("ragged", 2, "MOE_EINVAL"),
     ("E", 1024, "MOE_ESHAPE"),
+    ("T", 100000, "MOE_ESHAPE"),        # bf16 sorted rows 100000*6*2048*2 B > 2 GiB
 ])
 def test_validate_rejects(m, field, value, code):
     c = _cfgs(m)["dsv2lite"]
@@ -83,6 +84,14 @@ def test_validate_rejects(m, field, value, code):
     assert m.moe_validate(c) == getattr(m, code)
     assert m.moe_last_error()
     assert m.moe_workspace_bytes(c) == 0
+
+
+def test_validate_accepts_rows_just_below_the_offset_limit(m):
+    c = _cfgs(m)["dsv2lite"]
+    c.T = (2 ** 31 - 1) // (c.k_max * c.H * 2)     # 87381 tokens
+    assert m.moe_validate(c) == m.MOE_OK, m.moe_last_error()
+    c.T += 1
+    assert m.moe_validate(c) == m.MOE_ESHAPE
 
 
 def test_validate_sigmoid_group_rules(m):

@@ -14,20 +14,39 @@
 // chunks, one per XCD (workgroup i runs on XCD i % 8), so weight tiles are
 // reused from that XCD's L2.
 //
-// Tile 128 x 128 x 64, 256 threads (2 x 2 waves of 64 x 64), MFMA
-// 16x16x32 bf16, LDS double buffer.  LDS rows are 64 bf16 (128 bytes, eight
-// 16-byte chunks) stored with an XOR swizzle: chunk c of row r sits at chunk
-// position c ^ (r & 7).  Measured on gfx950, both the loader's row-wise
-// ds_write_b128 and the MFMA fragment ds_read_b128 (16 rows x one chunk) are
-// then free of bank conflicts, unlike a padded row stride.
+// Tiles are 256 x BN (BN = 256, or 128 when N does not split into 256-wide
+// tiles); the last m-tile of a segment with at most 128 rows left runs as a
+// 128 x BN tile.  Four waves in a 2 x 2 grid each own a (BM/2) x (BN/2)
+// block: at 256 x 256 that is 128 x 128 per wave, 8 x 8 MFMA 16x16x32 bf16
+// blocks with 256 fp32 accumulators per lane.  Large wave tiles keep the
+// LDS read traffic per flop low (each k-step reads (128 + 128) rows per wave
+// for 128 x 128 x 32 multiply-adds) and the 256 x 256 tile halves the bytes
+// fetched from L2 per flop compared with 128 x 256.
+//
+// Operands go HBM/L2 -> LDS directly (buffer_load_dwordx4 ... lds): no
+// staging registers and no ds_write instructions.  LDS holds two stages of
+// [A rows | B rows] with BK = 64: 128-byte rows (whole cache lines: with
+// 64-byte row pieces the L2 delivers half the bytes per cycle, measured),
+// eight 16-byte chunks per row, swizzled (see swz) so the fragment reads are
+// free of bank conflicts.  The swizzle is applied on the global side, since
+// each wave-wide LDS DMA writes 64 consecutive 16-byte slots.
+//
+// Pipeline per k-step (two MFMA k-halves of 32):
+//   wait for this wave's DMA of step kt, barrier
+//   read half 0's fragments, wait; read half 1's; MFMAs of half 0; wait
+//   barrier (every wave has read stage kt & 1); DMA step kt+2 into it
+//   MFMAs of half 1
+// so a DMA has about one and a half k-steps to land and up to two stages
+// (128 KB per CU) are in flight.
 #include "common.h"
 #include "internal.h"
 
 namespace moe {
 namespace {
 
-constexpr int BM = 128, BK = 64;
-constexpr int LDSK = BK;   // no padding: XOR-swizzled chunks
+constexpr int BM = 256, BK = 64, NS = 2;
+// waves along N (the wave grid is 2 x kWavesN)
+constexpr int kWavesN = 4;
 constexpr int kMaxSeg = 516;
 
 struct GemmParams {
@@ -77,62 +96,93 @@ MOE_DEV void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
-// LDS fragment read issued as inline asm: the compiler's wait-count pass then
-// does not treat it as a read of the in-flight LDS DMA (it would drain all
-// outstanding loads before it); completion is waited for explicitly with
-// frag_wait, whose operands tie the fragments so no use moves above it.
-// (The asm exists only in the device pass; the host pass never runs these.)
-MOE_DEV bf16x8_t lds_read_b128(const uint16_t* p)
+// Keeps two accumulator blocks in AGPRs up to this point of the program
+// order.  Without it the compiler hoists the epilogue's reads of all 256
+// accumulators into VGPRs at once and spills.
+MOE_DEV void acc_fence(f32x4_t& a, f32x4_t& b)
 {
 #if defined(__HIP_DEVICE_COMPILE__)
-    const uint32_t a = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const uint16_t*)p);
-    bf16x8_t v;
-    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(a));
-    return v;
-#else
-    return *(const bf16x8_t*)p;
-#endif
-}
-
-MOE_DEV void frag_wait(bf16x8_t (&a)[4], bf16x8_t (&b)[4])
-{
-#if defined(__HIP_DEVICE_COMPILE__)
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]),
-                   "+v"(b[2]), "+v"(b[3]));
+    asm volatile("" : "+a"(a), "+a"(b)::"memory");
 #else
     (void)a;
     (void)b;
 #endif
 }
 
-// Tile BM x BN x BK, BN/32 waves in a 2 x (BN/64) grid, each wave owning a
-// 64 x 64 block of the output (4 x 4 MFMA 16x16x32 tiles).  For the up
-// projection the BN columns are BN/2 gate neurons followed by the same BN/2
-// up neurons, and every wave holds matching gate and up columns so the SwiGLU
-// product is formed in registers.
-//
-// Operands go HBM/L2 -> LDS directly (buffer_load_dwordx4 ... lds): no
-// staging registers and no ds_write instructions.  LDS holds a ring of three
-// stages of [A tile | B tile]; rows are 128 bytes (eight 16-byte chunks),
-// XOR-swizzled (chunk c of row r at position c ^ (r & 7)), which keeps the
-// MFMA fragment reads free of bank conflicts; the swizzle is applied on the
-// global side, since each wave-wide LDS DMA writes 64 consecutive 16-byte
-// slots.  Each k-step: wait for this wave's DMA of tile kt, barrier, issue
-// the DMA of tile kt+2 into the stage read at step kt-1, compute tile kt.
-template <bool UP, int BN>
-__global__ __launch_bounds__(BN * 2, 1) void k_grouped_gemm(GemmParams p)
+template <int V>
+struct IntC {
+    static constexpr int value = V;
+};
+
+// Position of 16-byte chunk c of LDS row r (128-byte rows, eight chunks).
+// Bit 2 of the chunk (which 32-wide k-half) is kept, so the second half of a
+// fragment row is always 64 bytes after the first; the low two bits are
+// XORed with row bits 1-2.  Fragment reads (eight lanes per LDS cycle, rows
+// r..r+7 at one chunk) then hit eight distinct 16-byte bank groups.
+MOE_DEV int swz(int r, int c) { return (c & 4) | ((c ^ (r >> 1)) & 3); }
+
+// LDS fragment read issued as inline asm: the compiler's wait-count pass then
+// does not treat it as a read of the in-flight LDS DMA (it would drain all
+// outstanding loads before it); completion is waited for explicitly with
+// frag_wait, whose operands tie the fragments so no use moves above it.  The
+// fragment's position inside the stage is the instruction's immediate byte
+// offset, so one address register serves all fragments of an operand.
+// (The asm exists only in the device pass; the host pass never runs these.)
+template <int OFF>
+MOE_DEV bf16x8_t lds_read_b128(uint32_t addr)
 {
-    constexpr int kThreads = BN * 2;        // BN/32 waves
-    constexpr int NW = kThreads / 64;
-    constexpr int WN = BN / 64;             // waves along N
-    constexpr int NPT = BN / 2;             // up: neurons per tile
-    constexpr int kRows = BM + BN;          // 128-byte rows per stage
-    constexpr int kStageE = kRows * 64;     // bf16 elements per stage
-    constexpr int NS = 3;                   // LDS stages
-    constexpr int NI = kRows * 8 / 64 / NW; // DMA instructions per wave per stage
-    static_assert(kRows * 8 == NI * 64 * NW, "stage split");
-    static_assert(BM % 8 == 0, "a DMA instruction covers 8 rows of one operand");
+    static_assert(OFF >= 0 && OFF < 65536, "ds_read offset range");
+    bf16x8_t v;
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+#else
+    (void)addr;
+    v = bf16x8_t{};
+#endif
+    return v;
+}
+
+MOE_DEV uint32_t lds_addr(const void* p)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
+#else
+    return (uint32_t)(uintptr_t)p;
+#endif
+}
+
+template <int I, int N, typename F>
+MOE_DEV void static_for(F&& f)
+{
+    if constexpr (I < N) {
+        f(IntC<I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+template <int NA, int NB>
+MOE_DEV void frag_wait(bf16x8_t (&a)[NA], bf16x8_t (&b)[NB])
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < NA; ++i) asm volatile("" : "+v"(a[i]));
+#pragma unroll
+    for (int i = 0; i < NB; ++i) asm volatile("" : "+v"(b[i]));
+#else
+    (void)a;
+    (void)b;
+#endif
+}
+
+template <bool UP, int BN>
+__global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
+{
+    constexpr int NW = 2 * kWavesN;          // waves
+    constexpr int kThreads = 64 * NW;
+    constexpr int WC = BN / (16 * kWavesN);  // 16-column blocks per wave
+    constexpr int NPT = BN / 2;              // up: neurons per tile
+    constexpr int kStageE = (BM + BN) * BK;  // bf16 elements per stage
     __shared__ __attribute__((aligned(16))) uint16_t smem[NS * kStageE];
     __shared__ int s_pref[kMaxSeg + 1];
     __shared__ int s_row0[kMaxSeg];
@@ -141,7 +191,7 @@ __global__ __launch_bounds__(BN * 2, 1) void k_grouped_gemm(GemmParams p)
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
-    const int wm = w / WN, wn = w % WN;
+    const int wm = w / kWavesN, wn = w % kWavesN;
     const int nseg = p.n_routed + p.has_shared;
 
     // ---- tile list prefix over segments
@@ -224,146 +274,188 @@ __global__ __launch_bounds__(BN * 2, 1) void k_grouped_gemm(GemmParams p)
         const int b_bytes = (UP ? 2 * N : N) * K * 2;
         const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc((void*)Abase, (short)0, a_bytes, 0x00020000);
         const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc((void*)Bseg, (short)0, b_bytes, 0x00020000);
-        // DMA instruction jj of this wave covers stage rows [8(w*NI+jj), +8);
-        // lane l fills slot l: row 8(w*NI+jj) + l/8, position l%8, which holds
-        // the row's global chunk (l%8) ^ (row & 7).
-        int doff[NI];
-#pragma unroll
-        for (int jj = 0; jj < NI; ++jj) {
-            const int row = (w * NI + jj) * 8 + (l >> 3);
-            const int chunk = (l & 7) ^ (row & 7);
-            if (row < BM) {
-                const int gr = row0 + m0 + min(row, rows - 1);
-                const int src_row = (!shared && p.A == nullptr) ? p.row_tok[gr] : gr;
-                doff[jj] = src_row * K * 2 + chunk * 16;
-            } else {
-                const int r = row - BM;
-                int brow;
-                if (UP) {
-                    const int n0 = ntile * NPT;
-                    brow = r < NPT ? n0 + r : N + n0 + (r - NPT);
-                } else {
-                    brow = ntile * BN + r;
-                }
-                doff[jj] = brow * K * 2 + chunk * 16;
-            }
-        }
-        auto dma = [&](int kt, int st) {
-            const int ko = kt * BK * 2;
+        const int KT = K / BK;
+
+        // RT = 16-row blocks per wave: 8 for a 256-row tile, 4 for a tile of
+        // at most 128 rows (waves then own 64 rows each).
+        auto run_tile = [&](auto rt_tag) {
+            constexpr int RT = decltype(rt_tag)::value;
+            constexpr int kArows = RT * 32;                  // A rows loaded
+            constexpr int NA = kArows / 8;                   // A DMA instructions
+            constexpr int NI = (kArows + BN) / 8 / NW;       // DMA instructions per wave
+            static_assert((kArows + BN) % 32 == 0, "stage split");
+            // DMA instruction q = w*NI + jj covers 8 LDS rows; lane l fills
+            // row (l >> 3) of them at position l & 7, which holds the row's
+            // global chunk swz(row, l & 7) (the swizzle is an involution).
+            // The lane id is laundered through an empty asm so that the
+            // per-lane address arithmetic below stays inside the tile loop:
+            // hoisted out of it, its tile-invariant parts would occupy
+            // registers across the whole k-loop.
+            int lane = l;
+            asm volatile("" : "+v"(lane));
+            int doff[NI];
 #pragma unroll
             for (int jj = 0; jj < NI; ++jj) {
-                uint16_t* dst = smem + st * kStageE + (w * NI + jj) * 512;
+                const int q = w * NI + jj;
+                const int rin = lane >> 3;
+                const int chunk = swz(rin, lane & 7);
+                if (q < NA) {
+                    const int row = q * 8 + rin;
+                    const int gr = row0 + m0 + min(row, rows - 1);
+                    const int src_row = (!shared && p.A == nullptr) ? p.row_tok[gr] : gr;
+                    doff[jj] = src_row * K * 2 + chunk * 16;
+                } else {
+                    const int r = (q - NA) * 8 + rin;
+                    int brow;
+                    if (UP) {
+                        const int n0 = ntile * NPT;
+                        brow = r < NPT ? n0 + r : N + n0 + (r - NPT);
+                    } else {
+                        brow = ntile * BN + r;
+                    }
+                    doff[jj] = brow * K * 2 + chunk * 16;
+                }
+            }
+            auto dma = [&](int kt, int st) {
+                const int ko = kt * BK * 2;
+#pragma unroll
+                for (int jj = 0; jj < NI; ++jj) {
+                    const int q = w * NI + jj;
+                    uint16_t* dst = smem + st * kStageE + (q < NA ? q * 8 : BM + (q - NA) * 8) * BK;
 #if defined(__HIP_DEVICE_COMPILE__)  // the host pass cannot form LDS pointers
-                if ((w * NI + jj) * 8 < BM)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, MOE_LDS_PTR(dst), 16, doff[jj], ko, 0, 0);
-                else
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, MOE_LDS_PTR(dst), 16, doff[jj], ko, 0, 0);
+                    if (q < NA)
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, MOE_LDS_PTR(dst), 16, doff[jj], ko, 0, 0);
+                    else
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, MOE_LDS_PTR(dst), 16, doff[jj], ko, 0, 0);
 #else
-                (void)dst;
-                (void)ko;
+                    (void)dst;
+                    (void)ko;
 #endif
+                }
+            };
+
+            f32x4_t acc[RT][WC];
+#pragma unroll
+            for (int a = 0; a < RT; ++a)
+#pragma unroll
+                for (int b = 0; b < WC; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+            // Fragments of the two 32-wide k-halves of a stage.  Fragment rows
+            // are 16-row aligned, so the swizzled position depends on the lane
+            // only, and the second half sits 64 bytes after the first: one
+            // lane base per operand plus immediates.
+            bf16x8_t af0[RT], bf0[WC], af1[RT], bf1[WC];
+            const int lrow = lane & 15;
+            const uint32_t lane_off = lrow * (BK * 2) + (swz(lrow, lane >> 4) << 4);
+            const uint32_t a_base = lds_addr(smem) + lane_off + wm * (RT * 16) * (BK * 2);
+            const uint32_t b_base = lds_addr(smem) + lane_off + BM * (BK * 2) +
+                                    wn * (UP ? NPT / kWavesN : BN / kWavesN) * (BK * 2);
+            auto read = [&](int st, auto half, bf16x8_t (&af)[RT], bf16x8_t (&bfr)[WC]) {
+                constexpr int H0 = decltype(half)::value * 64;
+                const uint32_t so = st * (kStageE * 2);
+                const uint32_t ab = a_base + so, bb = b_base + so;
+                static_for<0, RT>([&](auto rt) {
+                    af[rt.value] = lds_read_b128<H0 + rt.value * 16 * (BK * 2)>(ab);
+                });
+                static_for<0, WC>([&](auto ct) {
+                    constexpr int c = ct.value;
+                    constexpr int cb = UP ? (c < WC / 2 ? c * 16 : NPT + (c - WC / 2) * 16) : c * 16;
+                    bfr[c] = lds_read_b128<H0 + cb * (BK * 2)>(bb);
+                });
+            };
+            auto mfma = [&](bf16x8_t (&af)[RT], bf16x8_t (&bfr)[WC]) {
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int ct = 0; ct < WC; ++ct)
+                        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[ct], af[rt], acc[rt][ct], 0, 0, 0);
+            };
+
+            // Two LDS stages of BK = 64.  Step kt: wait for this wave's DMA of
+            // step kt (at most the DMA of step kt+1 still in flight), barrier;
+            // read the first k-half's fragments, wait, read the second half's
+            // while the first half's MFMAs run, wait; barrier (every wave has
+            // read stage kt & 1); DMA step kt+2 into it; second half's MFMAs.
+            // A DMA thus has about one and a half k-steps to land, and up to
+            // two stages are in flight.
+            dma(0, 0);
+            if (KT > 1) dma(1, 1);
+            for (int kt = 0; kt < KT; ++kt) {
+                const int st = kt & 1;
+                if (kt + 1 < KT) wait_vmcnt<NI>(); else wait_vmcnt<0>();
+                __builtin_amdgcn_s_barrier();
+                read(st, IntC<0>{}, af0, bf0);
+                frag_wait(af0, bf0);
+                read(st, IntC<1>{}, af1, bf1);
+                mfma(af0, bf0);
+                frag_wait(af1, bf1);
+                __builtin_amdgcn_s_barrier();
+                if (kt + 2 < KT) dma(kt + 2, st);
+                mfma(af1, bf1);
+            }
+            __syncthreads();
+
+            // ---- epilogue.  The MFMAs compute the transposed tile (B rows as
+            // the first operand), so lane l holds output row (l & 15) and four
+            // consecutive output columns 4*(l >> 4) + v: packed into one
+            // 8-byte LDS store, then written out as 16-byte row chunks.
+            uint16_t* Cseg = shared ? p.shC : p.C;
+            constexpr int CW = UP ? NPT : BN / 2;  // output columns staged per pass
+            constexpr int CS = CW + 8;             // padded LDS row stride
+            constexpr int CPR = CW / 8;            // 16-byte chunks per staged row
+            constexpr int NPASS = UP ? 1 : 2;
+            uint16_t* Cs = smem;
+#pragma unroll
+            for (int pass = 0; pass < NPASS; ++pass) {
+                if (UP) {
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                        for (int c = 0; c < WC / 2; ++c) {
+                            acc_fence(acc[rt][c], acc[rt][c + WC / 2]);
+                            const int row = wm * (RT * 16) + rt * 16 + (l & 15);
+                            const f32x4_t g = acc[rt][c], u = acc[rt][c + WC / 2];
+                            uint2 v;
+                            v.x = pack2_bf16(silu_fast(g[0]) * u[0], silu_fast(g[1]) * u[1]);
+                            v.y = pack2_bf16(silu_fast(g[2]) * u[2], silu_fast(g[3]) * u[3]);
+                            *(uint2*)&Cs[row * CS + wn * (NPT / kWavesN) + c * 16 + (l >> 4) * 4] = v;
+                        }
+                } else {
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                        for (int c = 0; c < WC / 2; ++c) {
+                            acc_fence(acc[rt][pass * (WC / 2) + c], acc[rt][pass * (WC / 2) + c]);
+                            const int row = wm * (RT * 16) + rt * 16 + (l & 15);
+                            const f32x4_t a = acc[rt][pass * (WC / 2) + c];
+                            uint2 v;
+                            v.x = pack2_bf16(a[0], a[1]);
+                            v.y = pack2_bf16(a[2], a[3]);
+                            *(uint2*)&Cs[row * CS + wn * (BN / (2 * kWavesN)) + c * 16 + (l >> 4) * 4] = v;
+                        }
+                }
+                __syncthreads();
+#pragma unroll
+                for (int qq = 0; qq < (kArows * CPR) / kThreads; ++qq) {
+                    const int idx = tid + qq * kThreads;
+                    const int row = idx / CPR, ch = idx % CPR;
+                    int col;
+                    if (UP) {
+                        col = ntile * NPT + ch * 8;
+                    } else {
+                        constexpr int WPP = BN / (2 * kWavesN);  // columns per wave per pass
+                        const int lc = ch * 8, wv = lc / WPP;
+                        col = ntile * BN + wv * (BN / kWavesN) + pass * WPP + lc % WPP;
+                    }
+                    if (row < rows)
+                        *(u32x4_t*)&Cseg[(size_t)(row0 + m0 + row) * N + col] =
+                            *(const u32x4_t*)&Cs[row * CS + ch * 8];
+                }
+                __syncthreads();
             }
         };
-
-        f32x4_t acc[4][4];
-#pragma unroll
-        for (int a = 0; a < 4; ++a)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) acc[a][b] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-        auto compute = [&](int st) {
-            const uint16_t* As = smem + st * kStageE;
-            const uint16_t* Bs = As + BM * BK;
-            bf16x8_t af[2][4], bfr[2][4];
-            auto read = [&](int kk) {
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt) {
-                    const int row = wm * 64 + rt * 16 + (l & 15);
-                    af[kk][rt] = lds_read_b128(&As[row * BK + ((((kk << 2) + (l >> 4)) ^ (row & 7)) << 3)]);
-                }
-#pragma unroll
-                for (int ct = 0; ct < 4; ++ct) {
-                    const int cb = UP ? ((ct < 2) ? wn * 32 + ct * 16 : NPT + wn * 32 + (ct - 2) * 16)
-                                      : wn * 64 + ct * 16;
-                    const int row = cb + (l & 15);
-                    bfr[kk][ct] = lds_read_b128(&Bs[row * BK + ((((kk << 2) + (l >> 4)) ^ (row & 7)) << 3)]);
-                }
-            };
-            auto mfma = [&](int kk) {
-#pragma unroll
-                for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-                    for (int ct = 0; ct < 4; ++ct)
-                        acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bfr[kk][ct], af[kk][rt], acc[rt][ct], 0, 0, 0);
-            };
-            read(0);
-            frag_wait(af[0], bfr[0]);
-            read(1);             // overlaps the first half's MFMAs
-            mfma(0);
-            frag_wait(af[1], bfr[1]);
-            mfma(1);
-        };
-
-        const int KT = K / BK;
-        dma(0, 0);
-        if (KT > 1) dma(1, 1);
-        int st = 0;
-        for (int kt = 0; kt < KT; ++kt) {
-            // this wave's DMA of tile kt is done once at most the NI loads of
-            // tile kt+1 are still outstanding
-            if (kt + 1 < KT) wait_vmcnt<NI>(); else wait_vmcnt<0>();
-            __builtin_amdgcn_s_barrier();
-            if (kt + 2 < KT) dma(kt + 2, st == 0 ? 2 : st - 1);
-            compute(st);
-            st = st == 2 ? 0 : st + 1;
-        }
-        __syncthreads();
-
-        // ---- epilogue.  The MFMAs compute the transposed tile (B rows as
-        // the first operand), so lane l holds output row (l & 15) and four
-        // consecutive output columns 4*(l >> 4) + v: packed into one 8-byte
-        // LDS store, then written out as 16-byte row chunks.
-        uint16_t* Cseg = shared ? p.shC : p.C;
-        constexpr int CW = UP ? NPT : BN;  // output columns of the tile
-        constexpr int CS = CW + 8;         // padded LDS row stride
-        uint16_t* Cs = smem;
-        if (UP) {
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-                for (int c = 0; c < 2; ++c) {
-                    const int row = wm * 64 + rt * 16 + (l & 15);
-                    const f32x4_t g = acc[rt][c], u = acc[rt][c + 2];
-                    uint2 v;
-                    v.x = pack2_bf16(silu_fast(g[0]) * u[0], silu_fast(g[1]) * u[1]);
-                    v.y = pack2_bf16(silu_fast(g[2]) * u[2], silu_fast(g[3]) * u[3]);
-                    *(uint2*)&Cs[row * CS + wn * 32 + c * 16 + (l >> 4) * 4] = v;
-                }
-        } else {
-#pragma unroll
-            for (int rt = 0; rt < 4; ++rt)
-#pragma unroll
-                for (int ct = 0; ct < 4; ++ct) {
-                    const int row = wm * 64 + rt * 16 + (l & 15);
-                    const f32x4_t a = acc[rt][ct];
-                    uint2 v;
-                    v.x = pack2_bf16(a[0], a[1]);
-                    v.y = pack2_bf16(a[2], a[3]);
-                    *(uint2*)&Cs[row * CS + wn * 64 + ct * 16 + (l >> 4) * 4] = v;
-                }
-        }
-        __syncthreads();
-        constexpr int CPR = CW / 8;        // 16-byte chunks per row
-        const int n_out = UP ? ntile * NPT : ntile * BN;
-#pragma unroll
-        for (int q = 0; q < (BM * CPR) / kThreads; ++q) {
-            const int idx = tid + q * kThreads;
-            const int row = idx / CPR, ch = idx % CPR;
-            if (row < rows)
-                *(u32x4_t*)&Cseg[(size_t)(row0 + m0 + row) * N + n_out + ch * 8] =
-                    *(const u32x4_t*)&Cs[row * CS + ch * 8];
-        }
-        __syncthreads();
+        if (rows > BM / 2) run_tile(IntC<8>{});
+        else run_tile(IntC<4>{});
     }
 }
 
@@ -433,10 +525,10 @@ int num_cus()
 template <bool UP, int BN>
 hipError_t launch_gemm_t(const GemmParams& p, long long ub, hipStream_t s)
 {
-    // one resident block per CU (three LDS stages: 96 or 144 KB)
+    // one resident block per CU (four LDS stages: 96 or 128 KB)
     long long grid = std::min<long long>(ub, (long long)num_cus());
     grid = (grid + 7) / 8 * 8;
-    hipLaunchKernelGGL((k_grouped_gemm<UP, BN>), dim3((unsigned)grid), dim3(BN * 2), 0, s, p);
+    hipLaunchKernelGGL((k_grouped_gemm<UP, BN>), dim3((unsigned)grid), dim3(128 * kWavesN), 0, s, p);
     return hipGetLastError();
 }
 
@@ -476,6 +568,8 @@ hipError_t launch_gemm(const moe_cfg& c, const FfnArgs& a, bool up, hipStream_t 
         p.shK = a.Ish;
         p.shN = c.H;
     }
+    // the k-loop runs whole pairs of 32-wide k-steps
+    if (c.H % 64 != 0 || c.I % 64 != 0 || a.Ish % 64 != 0) return hipErrorInvalidValue;
     // wide tiles (BN = 256) when every segment's N splits into them
     const int nw_r = up ? 2 * c.I : c.H;
     const int nw_s = up ? 2 * a.Ish : c.H;
