@@ -124,6 +124,7 @@ WsLayout ws_layout(const moe_cfg& c)
     L.shuffle_need = off;
     L.h = take(A * c.I * es);
     L.h_sh = take(T * Ish * es);
+    L.gemm_ctr = take(16 * 4);
     L.ffn_need = off;
     L.x_sorted = c.fuse_gather ? off : take(A * c.H * es);
     L.y_sorted = take(A * c.H * es);
@@ -279,6 +280,7 @@ MOE_API int32_t moe_expert_ffn(const moe_cfg* cfg, int32_t which, const void* x_
     FfnArgs a;
     memset(&a, 0, sizeof(a));
     a.A_max = c.T * c.k_max;
+    a.ctr = at<int32_t>(ws, L.gemm_ctr);
     if (which == MOE_FFN_SHARED) {
         if (c.n_shared == 0) return fail(MOE_ESHAPE, "no shared experts in cfg");
         REQUIRE(x);
@@ -426,6 +428,7 @@ MOE_API int32_t moe_forward(const moe_cfg* cfg, const moe_weights* w, const moe_
     FfnArgs a;
     memset(&a, 0, sizeof(a));
     a.A_max = c.T * c.k_max;
+    a.ctr = at<int32_t>(ws, L.gemm_ctr);
     a.n_routed = c.T > 0 ? c.E : 0;
     a.e_begin = 0;
     a.expert_off = o.expert_off;

@@ -65,6 +65,7 @@ struct GemmParams {
     uint16_t* shC;           // up: h_sh [T, Ish]; down: y_sh [T, H]
     int shK, shN;
     int A_max;               // rows of the sorted row space (bounds of A, C)
+    int* ctr;                // [8] tile counters, one per XCD, zero at launch
 };
 
 MOE_DEV float silu(float g) { return g / (1.0f + expf(-g)); }
@@ -184,59 +185,112 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
     constexpr int NPT = BN / 2;              // up: neurons per tile
     constexpr int kStageE = (BM + BN) * BK;  // bf16 elements per stage
     __shared__ __attribute__((aligned(16))) uint16_t smem[NS * kStageE];
-    __shared__ int s_pref[kMaxSeg + 1];
+    __shared__ int s_pref[kMaxSeg + 1];   // tile index of each segment's first tile
+    __shared__ int s_wpref[kMaxSeg + 1];  // work before each segment
     __shared__ int s_row0[kMaxSeg];
     __shared__ int s_cnt[kMaxSeg];
     __shared__ int s_smem[17];
+    __shared__ int s_bound[2];
+    __shared__ int s_tile;
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
     const int wm = w / kWavesN, wn = w % kWavesN;
     const int nseg = p.n_routed + p.has_shared;
+    const int xcd = blockIdx.x & 7;
 
-    // ---- tile list prefix over segments
+    // ---- tile list over segments.  A tile's work is its k-steps, doubled
+    // for a 256-row tile (a tail tile of at most 128 rows counts once).
+    auto seg_geom = [&](int i, int& row0, int& cnt, int& nt, int& kt) {
+        if (i < p.n_routed) {
+            const int e = p.e_begin + i;
+            row0 = p.expert_off[e];
+            cnt = p.expert_off[e + 1] - row0;
+            nt = UP ? p.N / NPT : p.N / BN;
+            kt = p.K / BK;
+        } else {
+            row0 = 0;
+            cnt = p.T;
+            nt = UP ? p.shN / NPT : p.shN / BN;
+            kt = p.shK / BK;
+        }
+    };
+    auto ntile_work = [&](int cnt, int kt) {
+        const int mt = (cnt + BM - 1) / BM;
+        const int last = cnt - (mt - 1) * BM;
+        return ((mt - 1) * 2 + (last > BM / 2 ? 2 : 1)) * kt;
+    };
     {
         constexpr int SPT = (kMaxSeg + kThreads - 1) / kThreads;
-        int tiles[SPT], sum = 0;
+        int tiles[SPT], work[SPT], tsum = 0, wsum = 0;
 #pragma unroll
         for (int q = 0; q < SPT; ++q) {
             const int i = tid * SPT + q;
             tiles[q] = 0;
+            work[q] = 0;
             if (i < nseg) {
-                int row0, cnt, nt;
-                if (i < p.n_routed) {
-                    const int e = p.e_begin + i;
-                    row0 = p.expert_off[e];
-                    cnt = p.expert_off[e + 1] - row0;
-                    nt = UP ? p.N / NPT : p.N / BN;
-                } else {
-                    row0 = 0;
-                    cnt = p.T;
-                    nt = UP ? p.shN / NPT : p.shN / BN;
-                }
+                int row0, cnt, nt, kt;
+                seg_geom(i, row0, cnt, nt, kt);
                 s_row0[i] = row0;
                 s_cnt[i] = cnt;
                 tiles[q] = ((cnt + BM - 1) / BM) * nt;
+                work[q] = cnt > 0 ? nt * ntile_work(cnt, kt) : 0;
             }
-            sum += tiles[q];
+            tsum += tiles[q];
+            wsum += work[q];
         }
-        int total;
-        int run = block_excl_scan(sum, s_smem, &total);
+        int ttot, wtot;
+        int trun = block_excl_scan(tsum, s_smem, &ttot);
+        int wrun = block_excl_scan(wsum, s_smem, &wtot);
 #pragma unroll
         for (int q = 0; q < SPT; ++q) {
             const int i = tid * SPT + q;
-            if (i < nseg) s_pref[i] = run;
-            run += tiles[q];
+            if (i < nseg) {
+                s_pref[i] = trun;
+                s_wpref[i] = wrun;
+            }
+            trun += tiles[q];
+            wrun += work[q];
         }
-        if (tid == 0) s_pref[nseg] = total;
+        if (tid == 0) {
+            s_pref[nseg] = ttot;
+            s_wpref[nseg] = wtot;
+        }
+        __syncthreads();
+        // This XCD's share: the tiles whose work starts in
+        // [total * xcd / 8, total * (xcd + 1) / 8).  Workgroup i runs on XCD
+        // i % 8; the XCD's workgroups take its tiles in list order from a
+        // counter (tiles differ in length, so a static split would leave
+        // some workgroups idle at the end).
+        if (tid < 2) {
+            const long long target = ((long long)wtot * (xcd + tid)) >> 3;
+            int b = ttot;
+            if (target < wtot) {
+                int lo = 0, hi = nseg - 1;
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (s_wpref[mid] <= target) lo = mid; else hi = mid - 1;
+                }
+                int row0, cnt, nt, kt;
+                seg_geom(lo, row0, cnt, nt, kt);
+                const int mt = (cnt + BM - 1) / BM;
+                const int wn_ = ntile_work(cnt, kt);
+                const int rem = (int)(target - s_wpref[lo]);
+                const int n = rem / wn_;
+                const int m = min((rem % wn_) / (2 * kt), mt - 1);
+                b = s_pref[lo] + n * mt + m;
+            }
+            s_bound[tid] = b;
+        }
         __syncthreads();
     }
-    const int total = s_pref[nseg];
-    const int xcd = blockIdx.x & 7, G8 = gridDim.x >> 3, j = blockIdx.x >> 3;
-    const int L0 = (int)(((long long)total * xcd) >> 3);
-    const int L1 = (int)(((long long)total * (xcd + 1)) >> 3);
+    const int L0 = s_bound[0], L1 = s_bound[1];
 
-    for (int L = L0 + j; L < L1; L += G8) {
+    for (;;) {
+        if (tid == 0) s_tile = atomicAdd(&p.ctr[xcd], 1);
+        __syncthreads();
+        const int L = L0 + s_tile;
+        if (L >= L1) break;
         // ---- locate the tile
         int lo = 0, hi = nseg - 1;
         while (lo < hi) {
@@ -522,9 +576,15 @@ int num_cus()
     return cached[dev];
 }
 
+__global__ __launch_bounds__(64) void k_zero_ctr(int* ctr)
+{
+    if (threadIdx.x < 8) ctr[threadIdx.x] = 0;
+}
+
 template <bool UP, int BN>
 hipError_t launch_gemm_t(const GemmParams& p, long long ub, hipStream_t s)
 {
+    hipLaunchKernelGGL(k_zero_ctr, dim3(1), dim3(64), 0, s, p.ctr);
     // one resident block per CU (four LDS stages: 96 or 128 KB)
     long long grid = std::min<long long>(ub, (long long)num_cus());
     grid = (grid + 7) / 8 * 8;
@@ -541,6 +601,7 @@ hipError_t launch_gemm(const moe_cfg& c, const FfnArgs& a, bool up, hipStream_t 
     p.T = c.T;
     p.A_max = a.A_max;
     p.expert_off = a.expert_off;
+    p.ctr = a.ctr + (up ? 0 : 8);
     if (up) {
         p.A = (const uint16_t*)a.xs;
         p.X = (const uint16_t*)a.x;

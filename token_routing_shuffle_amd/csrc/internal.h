@@ -22,6 +22,7 @@ struct WsLayout {
     size_t expert_count, expert_off, group_count, group_off, pair_count;
     size_t tok_perm, tok_off, s2a, a2s, row_tok;  // shuffle outputs / scratch
     size_t x_sorted, h, h_sh, y_sorted, y_sh;     // expert FFN buffers
+    size_t gemm_ctr;                              // grouped-GEMM tile counters
     size_t shuffle_need, ffn_need, total;
     int nb;                                       // shuffle blocks
 };
@@ -72,6 +73,7 @@ struct FfnArgs {
     void* sh_h;                  // [T, Ish]
     void* sh_y;                  // [T, H]
     int Ish;                     // n_shared * I_shared
+    int32_t* ctr;                // [16] workspace tile counters (up: 0..7, down: 8..15)
 };
 hipError_t launch_ffn_up(const moe_cfg& c, const FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn_down(const moe_cfg& c, const FfnArgs& a, hipStream_t s);
