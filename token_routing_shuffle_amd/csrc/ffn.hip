@@ -27,8 +27,8 @@
 // staging registers and no ds_write instructions.  LDS holds two stages of
 // [A rows | B rows] with BK = 64: 128-byte rows (whole cache lines: with
 // 64-byte row pieces the L2 delivers half the bytes per cycle, measured),
-// eight 16-byte chunks per row, swizzled (see swz) so the fragment reads are
-// free of bank conflicts.  The swizzle is applied on the global side, since
+// eight 16-byte chunks per row, XOR-swizzled (see swz) so the fragment reads
+// are free of bank conflicts.  The swizzle is applied on the global side, since
 // each wave-wide LDS DMA writes 64 consecutive 16-byte slots.
 //
 // Pipeline per k-step (two MFMA k-halves of 32):
@@ -115,12 +115,10 @@ struct IntC {
     static constexpr int value = V;
 };
 
-// Position of 16-byte chunk c of LDS row r (128-byte rows, eight chunks).
-// Bit 2 of the chunk (which 32-wide k-half) is kept, so the second half of a
-// fragment row is always 64 bytes after the first; the low two bits are
-// XORed with row bits 1-2.  Fragment reads (eight lanes per LDS cycle, rows
-// r..r+7 at one chunk) then hit eight distinct 16-byte bank groups.
-MOE_DEV int swz(int r, int c) { return (c & 4) | ((c ^ (r >> 1)) & 3); }
+// Position of 16-byte chunk c of LDS row r (128-byte rows, eight chunks):
+// c ^ (r & 7).  Measured on gfx950, MFMA fragment reads (16 rows at one
+// chunk, for either 32-wide k-half) are then free of bank conflicts.
+MOE_DEV int swz(int r, int c) { return c ^ (r & 7); }
 
 // LDS fragment read issued as inline asm: the compiler's wait-count pass then
 // does not treat it as a read of the in-flight LDS DMA (it would drain all
@@ -396,25 +394,25 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
 
             // Fragments of the two 32-wide k-halves of a stage.  Fragment rows
             // are 16-row aligned, so the swizzled position depends on the lane
-            // only, and the second half sits 64 bytes after the first: one
-            // lane base per operand plus immediates.
+            // only: one lane base per operand and k-half plus immediates.
             bf16x8_t af0[RT], bf0[WC], af1[RT], bf1[WC];
             const int lrow = lane & 15;
-            const uint32_t lane_off = lrow * (BK * 2) + (swz(lrow, lane >> 4) << 4);
-            const uint32_t a_base = lds_addr(smem) + lane_off + wm * (RT * 16) * (BK * 2);
-            const uint32_t b_base = lds_addr(smem) + lane_off + BM * (BK * 2) +
-                                    wn * (UP ? NPT / kWavesN : BN / kWavesN) * (BK * 2);
+            const uint32_t a_row = lds_addr(smem) + (wm * (RT * 16) + lrow) * (BK * 2);
+            const uint32_t b_row = lds_addr(smem) + (BM + wn * (UP ? NPT / kWavesN : BN / kWavesN) + lrow) * (BK * 2);
+            const uint32_t c0 = swz(lrow, lane >> 4) << 4, c1 = swz(lrow, 4 + (lane >> 4)) << 4;
+            const uint32_t a_base[2] = {a_row + c0, a_row + c1};
+            const uint32_t b_base[2] = {b_row + c0, b_row + c1};
             auto read = [&](int st, auto half, bf16x8_t (&af)[RT], bf16x8_t (&bfr)[WC]) {
-                constexpr int H0 = decltype(half)::value * 64;
+                constexpr int h = decltype(half)::value;
                 const uint32_t so = st * (kStageE * 2);
-                const uint32_t ab = a_base + so, bb = b_base + so;
+                const uint32_t ab = a_base[h] + so, bb = b_base[h] + so;
                 static_for<0, RT>([&](auto rt) {
-                    af[rt.value] = lds_read_b128<H0 + rt.value * 16 * (BK * 2)>(ab);
+                    af[rt.value] = lds_read_b128<rt.value * 16 * (BK * 2)>(ab);
                 });
                 static_for<0, WC>([&](auto ct) {
                     constexpr int c = ct.value;
                     constexpr int cb = UP ? (c < WC / 2 ? c * 16 : NPT + (c - WC / 2) * 16) : c * 16;
-                    bfr[c] = lds_read_b128<H0 + cb * (BK * 2)>(bb);
+                    bfr[c] = lds_read_b128<cb * (BK * 2)>(bb);
                 });
             };
             auto mfma = [&](bf16x8_t (&af)[RT], bf16x8_t (&bfr)[WC]) {
