@@ -317,6 +317,36 @@ def combine(y_sorted, assign_to_sorted, row_ptr, w_flat, y_sh=None):
 
 
 # ----------------------------------------------------------------------------
+# one-GPU forms of the shuffled collectives around the MoE layer
+# ----------------------------------------------------------------------------
+
+def srs(x_part, tok_perm):
+    """Shuffled reduce-scatter, one-GPU form.
+
+    Under attention tensor parallelism every rank holds a partial sum of the
+    attention output for all T tokens; the reduce-scatter that follows is
+    reordered so that each rank receives the reduced rows of the tokens
+    predicted to need its experts (de technical summary §2B, ja technical
+    overview §2.2B: SRS).  With all P ranks' partials on one device the
+    result is the reduced [T, H] rows laid out in tok_perm order, rank g's
+    share being rows [tok_off[g], tok_off[g+1]):
+        y[i] = sum_p x_part[p, tok_perm[i]]            (fp64)
+    """
+    x = f64(x_part)
+    return x.sum(axis=0)[np.asarray(tok_perm, np.int64)]
+
+
+def sag(y, tok_perm):
+    """Shuffled all-gather, one-GPU form: the rows that the ranks hold in
+    tok_perm order are gathered and put back into token order (de §2B, ja
+    §2.2B: SAG):  out[tok_perm[i]] = y[i]  (bit copy)."""
+    y = np.asarray(y)
+    out = np.empty_like(y)
+    out[np.asarray(tok_perm, np.int64)] = y
+    return out
+
+
+# ----------------------------------------------------------------------------
 # offline table: token -> predicted expert group
 # ----------------------------------------------------------------------------
 

@@ -52,6 +52,12 @@ PY_MUTANTS = {
     "combine_shared_dropped": ("        out += f64(y_sh)", "        pass"),
     "shared_w3_from_w1": ("        W3 = Wsh13[nI:][r]", "        W3 = Wsh13[:nI][r]"),
     "lut_unseen_fallback": ("lut[unseen] = (np.arange(V)[unseen] % P).astype(np.int32)", "pass"),
+    "srs_inverse_permutation": ("return x.sum(axis=0)[np.asarray(tok_perm, np.int64)]",
+                                "return x.sum(axis=0)[np.argsort(np.asarray(tok_perm, np.int64))]"),
+    "srs_one_partial_only": ("return x.sum(axis=0)[np.asarray(tok_perm, np.int64)]",
+                             "return x[0][np.asarray(tok_perm, np.int64)]"),
+    "sag_gathers_instead_of_scattering": ("out[np.asarray(tok_perm, np.int64)] = y",
+                                          "out[:] = y[np.asarray(tok_perm, np.int64)]"),
 }
 
 

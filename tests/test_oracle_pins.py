@@ -506,3 +506,45 @@ def test_relative_error_metric():
     ref = np.array([[1.0, -4.0], [0.5, 0.25]])
     y = ref + np.array([[0.04, 0.0], [0.0, 0.01]])
     assert mo.relative_error(y, ref) == pytest.approx(0.02)
+
+
+# ---------------------------------------------------------------- SRS / SAG
+
+def test_srs_sag_golden():
+    g = read_golden("srs_sag_worked_example.txt")
+    T, H = int(g["T"][0]), int(g["H"][0])
+    perm = np.array([int(v) for v in g["tok_perm"]])
+    x = np.array([float(v) for v in g["x_part"]]).reshape(-1, T, H)
+    np.testing.assert_array_equal(mo.srs(x, perm).reshape(-1), [float(v) for v in g["srs"]])
+    z = np.array([float(v) for v in g["sag_in"]]).reshape(T, H)
+    np.testing.assert_array_equal(mo.sag(z, perm).reshape(-1), [float(v) for v in g["sag"]])
+
+
+@pytest.mark.parametrize("seed,P,T,H", [(0, 1, 7, 3), (1, 3, 11, 4), (2, 8, 5, 2), (3, 2, 0, 3)])
+def test_srs_sag_brute_force(seed, P, T, H):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((P, T, H))
+    perm = rng.permutation(T)
+    y = mo.srs(x, perm)
+    for i in range(T):                       # plain loops over the definition
+        for h in range(H):
+            acc = 0.0
+            for p in range(P):
+                acc += x[p, perm[i], h]
+            assert abs(y[i, h] - acc) <= 1e-12 * max(1.0, abs(acc))
+    out = mo.sag(y, perm)
+    for i in range(T):
+        np.testing.assert_array_equal(out[perm[i]], y[i])
+    # the all-gather undoes the shuffle: token t's row is the reduced row of t
+    for t in range(T):
+        red = sum(x[p, t] for p in range(P))
+        np.testing.assert_allclose(out[t], red, rtol=0, atol=1e-12)
+
+
+def test_srs_single_partial_is_a_row_permutation_and_sag_inverts_it():
+    rng = np.random.default_rng(9)
+    x = rng.integers(0, 1 << 16, size=(1, 6, 5)).astype(np.uint16)   # bf16 bit patterns
+    perm = np.array([4, 0, 5, 2, 1, 3])
+    y = mo.srs(x, perm)
+    np.testing.assert_array_equal(y, mo.f64(x[0])[perm])
+    np.testing.assert_array_equal(mo.sag(x[0][perm], perm), x[0])
