@@ -142,6 +142,8 @@ def main():
         if args.fuse_gather == 0 else None,
     }
 
+    srs_sag = time_srs_sag(cfg, c, tables, args, torch, np, moe, wl, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, tables, w, x, np, torch, min(args.cpu_sample, cfg.T))
@@ -169,9 +171,45 @@ def main():
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "secondary": secondary,
         "roofline": roofline,
+        "srs_sag": srs_sag,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+def time_srs_sag(cfg, c, tables, args, torch, np, moe, wl, dev):
+    """The one-GPU shuffled reduce-scatter (P tensor-parallel partials of the
+    layer input, reduced into predicted-group order) and shuffled all-gather
+    (layer output back to token order) on the same workload, timed apart from
+    the layer with HIP events; HBM roofline of each."""
+    T, H, P = cfg.T, cfg.H, cfg.P
+    b = 2 if cfg.dtype == "bf16" else 4
+    x_part = wl.make_partials(cfg, P, dev)
+    # tokens by (predicted group, token) for a v mod P table (any permutation
+    # moves the same bytes)
+    g = (tables.tok % P).astype(np.int64)
+    perm = torch.as_tensor(np.lexsort((np.arange(T), g)).astype(np.int32), device=dev)
+    y = torch.empty((T, H), dtype=x_part.dtype, device=dev)
+    out = torch.empty_like(y)
+    res = {}
+    for name, fn, nbytes in (
+            ("srs", lambda: moe.moe_srs(c, P, x_part, perm, y), P * T * H * b + T * H * b + 4 * T),
+            ("sag", lambda: moe.moe_sag(c, y, perm, out), 2 * T * H * b + 4 * T)):
+        for _ in range(args.warmup):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(args.steps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        ms = ev[0].elapsed_time(ev[1]) / args.steps
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[name] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes,
+                     "avg_launch_ms": round(ms, 4)}
+    res["partials"] = P
+    return res
 
 
 def copy_calibration(mb, torch, dev):

@@ -223,6 +223,41 @@ int32_t moe_combine(const moe_cfg* cfg, const void* y_sorted, const int32_t* ass
                     const int32_t* row_ptr, const float* topk_w, const void* y_sh, void* out,
                     void* stream);
 
+/*
+ * Shuffled reduce-scatter (SRS), one-GPU form.  Semantic Parallelism (de
+ * technical summary §2B, ja technical overview §2.2B): under attention tensor
+ * parallelism each of the P ranks holds a partial sum of the attention output
+ * for all T tokens; the reduce-scatter is reordered so that every rank
+ * receives the reduced rows of the tokens predicted to need its experts.
+ * With all partials on one device:
+ *     y[i] = sum_{p < n_part} x_part[p][tok_perm[i]]
+ * summed in fp32 in p order and rounded once to the dtype (bf16: RNE); rank
+ * g's share is rows [tok_off[g], tok_off[g+1]) (tok_perm, tok_off as
+ * produced by moe_shuffle).  Rows whose tok_perm entry lies outside [0, T)
+ * are written as zeros.
+ *   n_part           number of partials, 1..64;
+ *   x_part[n_part,T,H] partials (16-byte aligned);
+ *   tok_perm[T]      int32 token of each output row;
+ *   y[T,H]           output rows in tok_perm order (16-byte aligned).
+ * Errors: MOE_EINVAL (null or misaligned pointer, n_part out of range),
+ * configuration errors as moe_validate; MOE_EHIP on a launch failure.
+ */
+int32_t moe_srs(const moe_cfg* cfg, int32_t n_part, const void* x_part, const int32_t* tok_perm,
+                void* y, void* stream);
+
+/*
+ * Shuffled all-gather (SAG), one-GPU form (same passages): the rows the ranks
+ * hold in tok_perm order are gathered and restored to token order:
+ *     out[tok_perm[i]] = y[i]          (bit copy)
+ * Entries of tok_perm outside [0, T) are skipped; a tok_perm that is not a
+ * permutation leaves rows of out unwritten.
+ *   y[T,H] rows in tok_perm order; tok_perm[T]; out[T,H] token order (y and
+ *   out 16-byte aligned, not overlapping).
+ * Errors as moe_srs.
+ */
+int32_t moe_sag(const moe_cfg* cfg, const void* y, const int32_t* tok_perm, void* out,
+                void* stream);
+
 /* Device tensors of one layer for moe_forward (host struct of device pointers). */
 typedef struct moe_weights {
     const void* Wg;              /* [E,H] slot order */

@@ -29,7 +29,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "moe_combine", "moe_expert_ffn", "moe_forward", "moe_last_error", "moe_route",
-        "moe_shuffle", "moe_validate", "moe_workspace_bytes"])
+        "moe_sag", "moe_shuffle", "moe_srs", "moe_validate", "moe_workspace_bytes"])
 
 
 def test_library_exports_every_declared_symbol(m):
@@ -167,3 +167,21 @@ def test_empty_layer_validates(m):
     from token_routing_shuffle_amd import workload as wl
     c = m.make_cfg(wl.CONFIGS["tiny"], T=0)
     assert m.moe_validate(c) == m.MOE_OK
+
+
+def test_srs_sag_reject_bad_arguments_before_launching(m):
+    c = _cfgs(m)["dsv2lite"]
+    fake = ctypes.c_void_p(0x1000)      # never dereferenced: checks come first
+    odd = ctypes.c_void_p(0x1008)
+    assert m.lib().moe_srs(ctypes.byref(c), 0, fake, fake, fake, None) == m.MOE_EINVAL
+    assert m.lib().moe_srs(ctypes.byref(c), 65, fake, fake, fake, None) == m.MOE_EINVAL
+    assert m.lib().moe_srs(ctypes.byref(c), 8, None, fake, fake, None) == m.MOE_EINVAL
+    assert m.lib().moe_srs(ctypes.byref(c), 8, odd, fake, fake, None) == m.MOE_EINVAL
+    assert m.lib().moe_sag(ctypes.byref(c), fake, None, fake, None) == m.MOE_EINVAL
+    assert m.lib().moe_sag(ctypes.byref(c), fake, fake, fake, None) == m.MOE_EINVAL   # y == out
+    bad = _cfgs(m)["dsv2lite"]
+    bad.P = 3
+    assert m.lib().moe_sag(ctypes.byref(bad), fake, fake, fake, None) == m.MOE_ESHAPE
+    empty = _cfgs(m)["dsv2lite"]
+    empty.T = 0                          # nothing to do, nothing touched
+    assert m.lib().moe_srs(ctypes.byref(empty), 8, None, None, None, None) == m.MOE_OK

@@ -346,6 +346,40 @@ MOE_API int32_t moe_combine(const moe_cfg* cfg, const void* y_sorted,
     return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_combine");
 }
 
+MOE_API int32_t moe_srs(const moe_cfg* cfg, int32_t n_part, const void* x_part,
+                        const int32_t* tok_perm, void* y, void* stream)
+{
+    int32_t rc = check_cfg(cfg);
+    if (rc != MOE_OK) return rc;
+    const moe_cfg& c = *cfg;
+    if (n_part < 1 || n_part > 64) return fail(MOE_EINVAL, "n_part must be in [1, 64]");
+    if (c.T == 0) return MOE_OK;
+    REQUIRE(x_part);
+    REQUIRE(tok_perm);
+    REQUIRE(y);
+    REQUIRE16(x_part);
+    REQUIRE16(y);
+    hipError_t e = launch_srs(c, n_part, x_part, tok_perm, y, (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_srs");
+}
+
+MOE_API int32_t moe_sag(const moe_cfg* cfg, const void* y, const int32_t* tok_perm, void* out,
+                        void* stream)
+{
+    int32_t rc = check_cfg(cfg);
+    if (rc != MOE_OK) return rc;
+    const moe_cfg& c = *cfg;
+    if (c.T == 0) return MOE_OK;
+    REQUIRE(y);
+    REQUIRE(tok_perm);
+    REQUIRE(out);
+    REQUIRE16(y);
+    REQUIRE16(out);
+    if (y == out) return fail(MOE_EINVAL, "y and out must not overlap");
+    hipError_t e = launch_sag(c, y, tok_perm, out, (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_sag");
+}
+
 MOE_API int32_t moe_forward(const moe_cfg* cfg, const moe_weights* w, const moe_inputs* in,
                             void* out, const moe_exports* ex, void* ws, size_t ws_bytes,
                             void* stream)

@@ -82,4 +82,9 @@ hipError_t launch_combine(const moe_cfg& c, const void* y_sorted, const int32_t*
                           const int32_t* row_ptr, const float* topk_w, const void* y_sh,
                           void* out, hipStream_t s);
 
+hipError_t launch_srs(const moe_cfg& c, int n_part, const void* x_part, const int32_t* tok_perm,
+                      void* y, hipStream_t s);
+hipError_t launch_sag(const moe_cfg& c, const void* y, const int32_t* tok_perm, void* out,
+                      hipStream_t s);
+
 }  // namespace moe

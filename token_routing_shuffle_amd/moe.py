@@ -86,6 +86,10 @@ def _load():
     lib.moe_expert_ffn.argtypes = [P(moe_cfg), i32] + [vp] * 7 + [i32, i32, vp, vp, sz, vp]
     lib.moe_combine.restype = i32
     lib.moe_combine.argtypes = [P(moe_cfg)] + [vp] * 7
+    lib.moe_srs.restype = i32
+    lib.moe_srs.argtypes = [P(moe_cfg), i32, vp, vp, vp, vp]
+    lib.moe_sag.restype = i32
+    lib.moe_sag.argtypes = [P(moe_cfg), vp, vp, vp, vp]
     lib.moe_forward.restype = i32
     lib.moe_forward.argtypes = [P(moe_cfg), P(moe_weights), P(moe_inputs), vp, P(moe_exports),
                                 vp, sz, vp]
@@ -103,7 +107,7 @@ def lib():
 
 
 EXPORTED = ("moe_validate", "moe_workspace_bytes", "moe_last_error", "moe_route", "moe_shuffle",
-            "moe_expert_ffn", "moe_combine", "moe_forward")
+            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_srs", "moe_sag")
 
 
 def _p(t) -> Optional[int]:
@@ -201,6 +205,17 @@ def moe_combine(cfg, y_sorted, assign_to_sorted, row_ptr, topk_w, y_sh, out, str
     rc = lib().moe_combine(ctypes.byref(cfg), _p(y_sorted), _p(assign_to_sorted), _p(row_ptr),
                            _p(topk_w), _p(y_sh), _p(out), _stream(stream))
     _check(rc, "moe_combine")
+
+
+def moe_srs(cfg, n_part, x_part, tok_perm, y, stream=None):
+    rc = lib().moe_srs(ctypes.byref(cfg), int(n_part), _p(x_part), _p(tok_perm), _p(y),
+                       _stream(stream))
+    _check(rc, "moe_srs")
+
+
+def moe_sag(cfg, y, tok_perm, out, stream=None):
+    rc = lib().moe_sag(ctypes.byref(cfg), _p(y), _p(tok_perm), _p(out), _stream(stream))
+    _check(rc, "moe_sag")
 
 
 def moe_forward(cfg, weights: moe_weights, inputs: moe_inputs, out, exports=None, ws=None,

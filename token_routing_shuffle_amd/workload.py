@@ -32,7 +32,7 @@ import numpy as np
 
 # Order of the child seed streams spawned from SeedSequence([2026, c]).
 STREAMS = ("placement", "tokens", "pref", "prof_tokens", "prof_x", "x", "Wg",
-           "ebias", "W13", "W2", "shared", "k_req")
+           "ebias", "W13", "W2", "shared", "k_req", "partials")
 
 PROFILE_TOKENS = 65536
 
@@ -223,6 +223,16 @@ def make_x(cfg: LayerConfig, device="cpu", n: Optional[int] = None, stream="x"):
     T_draw = _DRAW_T.get(cfg.name, n) if stream == "x" else n
     x = _randn((max(T_draw, n), cfg.H), 1.0, _gen(st[stream], device), device, cfg.dtype)
     return x[:n].contiguous() if x.shape[0] != n else x
+
+
+def make_partials(cfg: LayerConfig, n_part: int, device="cpu", n: Optional[int] = None):
+    """Tensor-parallel partial sums x_part[n_part, n, H] of an attention
+    output, each ~ N(0, 1/n_part) so that their sum is ~ N(0, 1)
+    (bf16-rounded unless fp32)."""
+    st = _streams(cfg)
+    n = cfg.T if n is None else n
+    return _randn((n_part, n, cfg.H), n_part ** -0.5, _gen(st["partials"], device), device,
+                  cfg.dtype)
 
 
 def make_weights(cfg: LayerConfig, device="cpu"):
