@@ -251,6 +251,7 @@ MOE_API int32_t moe_shuffle(const moe_cfg* cfg, const int32_t* row_ptr, const in
     o.g_pred = at<int32_t>(ws, L.g_pred);
     o.hist = at<int32_t>(ws, L.hist);
     o.thist = at<int32_t>(ws, L.thist);
+    o.gemm_ctr = nullptr;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_shuffle(c, L.nb, row_ptr, topk_slot, tok, lut, o, s);
     if (e == hipSuccess && x_sorted != nullptr) e = launch_gather(c, x, row_ptr, assign_to_sorted, x_sorted, s);
@@ -434,6 +435,7 @@ MOE_API int32_t moe_forward(const moe_cfg* cfg, const moe_weights* w, const moe_
     o.g_pred = at<int32_t>(ws, L.g_pred);
     o.hist = at<int32_t>(ws, L.hist);
     o.thist = at<int32_t>(ws, L.thist);
+    o.gemm_ctr = at<int32_t>(ws, L.gemm_ctr);   // zeroed by the shuffle for the FFN below
     void* x_sorted = c.fuse_gather ? nullptr : (X->x_sorted ? X->x_sorted : at<void>(ws, L.x_sorted));
     void* y_sorted = X->y_sorted ? X->y_sorted : at<void>(ws, L.y_sorted);
     void* y_sh = c.n_shared > 0 ? (X->y_shared ? X->y_shared : at<void>(ws, L.y_sh)) : nullptr;
@@ -463,6 +465,7 @@ MOE_API int32_t moe_forward(const moe_cfg* cfg, const moe_weights* w, const moe_
     memset(&a, 0, sizeof(a));
     a.A_max = c.T * c.k_max;
     a.ctr = at<int32_t>(ws, L.gemm_ctr);
+    a.ctr_zeroed = true;
     a.n_routed = c.T > 0 ? c.E : 0;
     a.e_begin = 0;
     a.expert_off = o.expert_off;

@@ -576,13 +576,12 @@ int num_cus()
 
 __global__ __launch_bounds__(64) void k_zero_ctr(int* ctr)
 {
-    if (threadIdx.x < 8) ctr[threadIdx.x] = 0;
+    if (threadIdx.x < 16) ctr[threadIdx.x] = 0;
 }
 
 template <bool UP, int BN>
 hipError_t launch_gemm_t(const GemmParams& p, long long ub, hipStream_t s)
 {
-    hipLaunchKernelGGL(k_zero_ctr, dim3(1), dim3(64), 0, s, p.ctr);
     // one resident block per CU (four LDS stages: 96 or 128 KB)
     long long grid = std::min<long long>(ub, (long long)num_cus());
     grid = (grid + 7) / 8 * 8;
@@ -600,6 +599,8 @@ hipError_t launch_gemm(const moe_cfg& c, const FfnArgs& a, bool up, hipStream_t 
     p.A_max = a.A_max;
     p.expert_off = a.expert_off;
     p.ctr = a.ctr + (up ? 0 : 8);
+    // both GEMMs' counters are zeroed once, before the up projection
+    if (up && !a.ctr_zeroed) hipLaunchKernelGGL(k_zero_ctr, dim3(1), dim3(64), 0, s, a.ctr);
     if (up) {
         p.A = (const uint16_t*)a.xs;
         p.X = (const uint16_t*)a.x;

@@ -41,6 +41,7 @@ struct ShuffleOut {
     int32_t *expert_count, *expert_off, *group_count, *group_off, *pair_count;
     int32_t *tok_perm, *tok_off, *s2a, *a2s, *row_tok;
     int32_t *g_pred, *hist, *thist;
+    int32_t* gemm_ctr;  // [16] grouped-GEMM tile counters to zero, or nullptr
 };
 hipError_t launch_shuffle(const moe_cfg& c, int nb, const int32_t* row_ptr,
                           const int32_t* topk_slot, const int32_t* tok, const int32_t* lut,
@@ -74,6 +75,7 @@ struct FfnArgs {
     void* sh_y;                  // [T, H]
     int Ish;                     // n_shared * I_shared
     int32_t* ctr;                // [16] workspace tile counters (up: 0..7, down: 8..15)
+    bool ctr_zeroed;             // ctr already zero on the stream (else the up GEMM zeroes it)
 };
 hipError_t launch_ffn_up(const moe_cfg& c, const FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn_down(const moe_cfg& c, const FfnArgs& a, hipStream_t s);

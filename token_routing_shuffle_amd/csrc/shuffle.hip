@@ -102,6 +102,8 @@ MOE_DEV int block_scan_inplace(int32_t* a, int n, int* smem)
 
 __global__ __launch_bounds__(1024) void k_scan(ShParams p)
 {
+    // the grouped GEMMs' tile counters start from zero for the layer
+    if (p.o.gemm_ctr != nullptr && threadIdx.x < 16) p.o.gemm_ctr[threadIdx.x] = 0;
     __shared__ int smem[17];
     __shared__ int s_total;
     const int n = p.nbk * p.nb;
