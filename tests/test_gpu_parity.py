@@ -398,3 +398,37 @@ def test_ffn_group_share_matches_full():
                          g * epg, (g + 1) * epg, parts, ws)
     torch.cuda.synchronize()
     assert torch.equal(full[:A], parts[:A])
+
+
+@pytest.mark.parametrize("name", ["dsv2lite_1000", "prism_1000"])
+def test_ffn_every_tile_height(name):
+    """Expert row counts chosen so that the last m-tile of a segment takes
+    each tile height (64, 128, 192, 256 rows) and the edges around them; the
+    GEMMs are checked row by row against the oracle's expert FFN."""
+    c = case(name)
+    m = moe_mod()
+    E, H = c.cfg.E, c.cfg.H
+    counts = [1, 63, 64, 65, 127, 128, 129, 191, 192, 193, 255, 256, 257, 300, 0, 511, 513]
+    counts = (counts + [0] * E)[:E]
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    A = int(off[-1])
+    cfg_t = c.cfg.replace(T=(A + c.cfg.k - 1) // c.cfg.k)
+    cfg = m.make_cfg(cfg_t)
+    rng = np.random.default_rng(11)
+    xs_h = hn.bf16_bits(rng.standard_normal((A, H)))
+    xs = torch.zeros((cfg_t.T * cfg_t.k, H), dtype=torch.bfloat16, device=hn.DEV)
+    xs[:A] = hn.to_dev(xs_h)
+    y = torch.zeros_like(xs)
+    print("[ffn] tile heights", name, A, flush=True)
+    m.moe_expert_ffn(cfg, m.MOE_FFN_ROUTED, xs, None, None, None, hn.to_dev(off), c.dev["W13"],
+                     c.dev["W2"], 0, E, y, m.workspace(cfg))
+    torch.cuda.synchronize()
+    yh = hn.f64_of(hn.host(y))[:A]
+    for s in range(E):
+        r0, r1 = off[s], off[s + 1]
+        if r1 > r0:
+            ref = mo.expert_ffn(mo.f64(xs_h[r0:r1]), c.h["W13"], c.h["W2"],
+                                int(c.tables.slot_to_orig[s]), c.cfg.I)
+            err = hn.rel_err(yh[r0:r1], ref)
+            assert err <= hn.tol_out(c.cfg), (s, counts[s], err)
+    assert not y[A:].any()

@@ -15,13 +15,12 @@
 // reused from that XCD's L2.
 //
 // Tiles are 256 x BN (BN = 256, or 128 when N does not split into 256-wide
-// tiles); the last m-tile of a segment with at most 128 rows left runs as a
-// 128 x BN tile.  Four waves in a 2 x 2 grid each own a (BM/2) x (BN/2)
-// block: at 256 x 256 that is 128 x 128 per wave, 8 x 8 MFMA 16x16x32 bf16
-// blocks with 256 fp32 accumulators per lane.  Large wave tiles keep the
-// LDS read traffic per flop low (each k-step reads (128 + 128) rows per wave
-// for 128 x 128 x 32 multiply-adds) and the 256 x 256 tile halves the bytes
-// fetched from L2 per flop compared with 128 x 256.
+// tiles); the last m-tile of a segment runs with the smallest height of 64,
+// 128, 192 or 256 rows that covers its rows, so at most 63 rows of MFMA work
+// are padding.  Eight waves in a 2 x 4 grid each own a (BM/2) x (BN/4) block:
+// at 256 x 256 that is 128 x 64 per wave, 8 x 4 MFMA 16x16x32 bf16 blocks
+// with 128 fp32 accumulators per lane, two waves per SIMD.  The 256 x 256
+// tile fetches 2/3 of the L2 bytes per flop of a 128 x 256 tile.
 //
 // Operands go HBM/L2 -> LDS directly (buffer_load_dwordx4 ... lds): no
 // staging registers and no ds_write instructions.  LDS holds two stages of
@@ -197,8 +196,8 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
     const int nseg = p.n_routed + p.has_shared;
     const int xcd = blockIdx.x & 7;
 
-    // ---- tile list over segments.  A tile's work is its k-steps, doubled
-    // for a 256-row tile (a tail tile of at most 128 rows counts once).
+    // ---- tile list over segments.  A tile's work is its k-steps times its
+    // height in 64-row units.
     auto seg_geom = [&](int i, int& row0, int& cnt, int& nt, int& kt) {
         if (i < p.n_routed) {
             const int e = p.e_begin + i;
@@ -216,7 +215,7 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
     auto ntile_work = [&](int cnt, int kt) {
         const int mt = (cnt + BM - 1) / BM;
         const int last = cnt - (mt - 1) * BM;
-        return ((mt - 1) * 2 + (last > BM / 2 ? 2 : 1)) * kt;
+        return ((mt - 1) * 4 + (last + 63) / 64) * kt;
     };
     {
         constexpr int SPT = (kMaxSeg + kThreads - 1) / kThreads;
@@ -275,7 +274,7 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
                 const int wn_ = ntile_work(cnt, kt);
                 const int rem = (int)(target - s_wpref[lo]);
                 const int n = rem / wn_;
-                const int m = min((rem % wn_) / (2 * kt), mt - 1);
+                const int m = min((rem % wn_) / (4 * kt), mt - 1);
                 b = s_pref[lo] + n * mt + m;
             }
             s_bound[tid] = b;
@@ -328,8 +327,8 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
         const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc((void*)Bseg, (short)0, b_bytes, 0x00020000);
         const int KT = K / BK;
 
-        // RT = 16-row blocks per wave: 8 for a 256-row tile, 4 for a tile of
-        // at most 128 rows (waves then own 64 rows each).
+        // RT = 16-row blocks per wave: the tile has 32 * RT rows (RT = 8, 6,
+        // 4 or 2), split between the two wave rows.
         auto run_tile = [&](auto rt_tag) {
             constexpr int RT = decltype(rt_tag)::value;
             constexpr int kArows = RT * 32;                  // A rows loaded
@@ -506,8 +505,10 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
                 __syncthreads();
             }
         };
-        if (rows > BM / 2) run_tile(IntC<8>{});
-        else run_tile(IntC<4>{});
+        if (rows > 192) run_tile(IntC<8>{});
+        else if (rows > 128) run_tile(IntC<6>{});
+        else if (rows > 64) run_tile(IntC<4>{});
+        else run_tile(IntC<2>{});
     }
 }
 
