@@ -366,10 +366,131 @@ def build_lut(prof_tok, prof_sel_orig, perm, E: int, P: int, V: int) -> np.ndarr
     v = np.asarray(prof_tok)[t_idx]
     cnt = np.zeros((V, P), np.int64)
     np.add.at(cnt, (v, g), 1)
-    lut = np.argmax(cnt, axis=1).astype(np.int32)    # first maximum = lowest g
-    unseen = cnt.sum(axis=1) == 0
+    return lut_from_counts(cnt)
+
+
+# ----------------------------------------------------------------------------
+# offline co-scheduling: expert placement and request placement
+# ----------------------------------------------------------------------------
+#
+# The pages pose expert placement and token/request scheduling as one 0-1
+# co-clustering problem (experts and tokens into P device groups, maximising
+# the work that stays local under balanced groups) solved by alternating
+# optimisation (de technical summary §2B and key contribution 4; ko technical
+# summary §2.2.1; ja technical overview §2.2A).  Reading taken: the objective
+# is the number of profiled assignments whose token is predicted for the
+# group holding its expert, sum_a [lut[tok_a] == group[expert_a]]; the two
+# alternating steps each maximise it exactly with the other side fixed:
+#   token step   lut[v] = argmax_g (assignments of token ID v on group g's
+#                experts), ties to the lower group, unseen IDs v mod P;
+#   expert step  group[] = the assignment of experts to groups, E/P experts
+#                per group, maximising sum_e count[group[e]][e], where
+#                count[g][e] = assignments at expert e of tokens with lut = g.
+# Experts are original ids here (profiling runs with the identity placement).
+
+def _assignment_token_ids(row_ptr, tok):
+    row_ptr = np.asarray(row_ptr, np.int64)
+    T = len(row_ptr) - 1
+    return np.asarray(tok, np.int64)[np.repeat(np.arange(T), np.diff(row_ptr))]
+
+
+def token_group_counts(row_ptr, expert, tok, group, V: int, P: int) -> np.ndarray:
+    """D[v][g] = profiled assignments of token ID v to experts of group g."""
+    A = int(np.asarray(row_ptr)[-1])
+    v = _assignment_token_ids(row_ptr, tok)
+    g = np.asarray(group, np.int64)[np.asarray(expert, np.int64)[:A]]
+    D = np.zeros((V, P), np.int64)
+    np.add.at(D, (v, g), 1)
+    return D
+
+
+def lut_from_counts(D: np.ndarray) -> np.ndarray:
+    """Token step: lut[v] = argmax_g D[v][g] (lowest g on ties), unseen -> v mod P."""
+    V, P = D.shape
+    lut = np.argmax(D, axis=1).astype(np.int32)      # first maximum = lowest g
+    unseen = D.sum(axis=1) == 0
     lut[unseen] = (np.arange(V)[unseen] % P).astype(np.int32)
     return lut
+
+
+def expert_group_counts(row_ptr, expert, tok, lut, E: int, P: int) -> np.ndarray:
+    """count[g][e] = profiled assignments at expert e of tokens with lut[tok] = g."""
+    A = int(np.asarray(row_ptr)[-1])
+    g = np.asarray(lut, np.int64)[_assignment_token_ids(row_ptr, tok)]
+    cnt = np.zeros((P, E), np.int64)
+    np.add.at(cnt, (g, np.asarray(expert, np.int64)[:A]), 1)
+    return cnt
+
+
+def balanced_assign(score: np.ndarray) -> np.ndarray:
+    """Items to groups, n/P items per group, maximising sum_i score[i, group[i]].
+
+    score is [n, P] with P dividing n.  Each group is given n/P identical
+    slots and the n x n assignment problem is solved exactly (a library
+    linear-assignment routine).  Returns group[i]."""
+    from scipy.optimize import linear_sum_assignment
+    n, P = score.shape
+    cap = n // P
+    cost = -np.repeat(np.asarray(score, np.float64), cap, axis=1)
+    rows, cols = linear_sum_assignment(cost)
+    group = np.empty(n, np.int32)
+    group[rows] = (cols // cap).astype(np.int32)
+    return group
+
+
+def local_count(row_ptr, expert, tok, group, lut) -> int:
+    """Objective: assignments whose token is predicted for its expert's group."""
+    A = int(np.asarray(row_ptr)[-1])
+    gt = np.asarray(lut, np.int64)[_assignment_token_ids(row_ptr, tok)]
+    ge = np.asarray(group, np.int64)[np.asarray(expert, np.int64)[:A]]
+    return int((gt == ge).sum())
+
+
+def optimize_placement(row_ptr, expert, tok, group0, V: int, E: int, P: int, max_iters: int = 20):
+    """Alternate token and expert steps from the expert grouping group0 until
+    the grouping repeats.  Returns (group, lut, objective after each step)."""
+    group = np.asarray(group0, np.int32).copy()
+    trace = []
+    lut = None
+    for _ in range(max_iters):
+        lut = lut_from_counts(token_group_counts(row_ptr, expert, tok, group, V, P))
+        trace.append(local_count(row_ptr, expert, tok, group, lut))
+        new = balanced_assign(expert_group_counts(row_ptr, expert, tok, lut, E, P).T)
+        trace.append(local_count(row_ptr, expert, tok, new, lut))
+        if trace[-1] <= trace[-2]:
+            break                    # no strict gain: keep the previous grouping
+        group = new
+    lut = lut_from_counts(token_group_counts(row_ptr, expert, tok, group, V, P))
+    return group, lut, trace
+
+
+def placement_of_groups(group, P: int) -> np.ndarray:
+    """perm[orig] = slot: group g's experts take slots [g*E/P, (g+1)*E/P) in
+    ascending original id."""
+    group = np.asarray(group, np.int64)
+    order = np.lexsort((np.arange(len(group)), group))
+    perm = np.empty(len(group), np.int32)
+    perm[order] = np.arange(len(group), dtype=np.int32)
+    return perm
+
+
+def request_group_hist(req_ptr, tok, lut, P: int) -> np.ndarray:
+    """Inter-request scheduling under attention data parallelism: H[r][g] =
+    tokens of request r (tokens [req_ptr[r], req_ptr[r+1])) predicted for
+    group g (de technical summary §2B; ko technical summary §2.2.2)."""
+    req_ptr = np.asarray(req_ptr, np.int64)
+    R = len(req_ptr) - 1
+    r_of_t = np.repeat(np.arange(R), np.diff(req_ptr))
+    g = np.asarray(lut, np.int64)[np.asarray(tok, np.int64)[:req_ptr[-1]]]
+    H = np.zeros((R, P), np.int64)
+    np.add.at(H, (r_of_t, g), 1)
+    return H
+
+
+def assign_requests(H: np.ndarray) -> np.ndarray:
+    """Requests to data-parallel ranks, R/P per rank, maximising the tokens
+    whose predicted group is their rank's: balanced_assign on H."""
+    return balanced_assign(H)
 
 
 def relative_error(y, ref) -> float:

@@ -58,6 +58,16 @@ PY_MUTANTS = {
                              "return x[0][np.asarray(tok_perm, np.int64)]"),
     "sag_gathers_instead_of_scattering": ("out[np.asarray(tok_perm, np.int64)] = y",
                                           "out[:] = y[np.asarray(tok_perm, np.int64)]"),
+    "balanced_assign_minimises": ("cost = -np.repeat(np.asarray(score, np.float64), cap, axis=1)",
+                                  "cost = np.repeat(np.asarray(score, np.float64), cap, axis=1)"),
+    "lut_ties_to_higher_group": ("lut = np.argmax(D, axis=1).astype(np.int32)",
+                                 "lut = (P - 1 - np.argmax(D[:, ::-1], axis=1)).astype(np.int32)"),
+    "expert_counts_use_expert_group": ("g = np.asarray(lut, np.int64)[_assignment_token_ids(row_ptr, tok)]\n    cnt",
+                                       "g = np.asarray(lut, np.int64)[np.asarray(expert, np.int64)[:A] % len(lut)]\n    cnt"),
+    "slots_descending_ids": ("order = np.lexsort((np.arange(len(group)), group))",
+                             "order = np.lexsort((-np.arange(len(group)), group))"),
+    "request_hist_by_token_index": ("g = np.asarray(lut, np.int64)[np.asarray(tok, np.int64)[:req_ptr[-1]]]",
+                                    "g = np.asarray(lut, np.int64)[np.arange(req_ptr[-1]) % len(lut)]"),
 }
 
 

@@ -2,6 +2,7 @@
 hand-worked fixtures (tests/golden), closed forms, library routines the oracle
 does not use, brute force on tiny inputs, and invariants the pages fix.
 """
+import itertools
 import math
 import os
 
@@ -548,3 +549,109 @@ def test_srs_single_partial_is_a_row_permutation_and_sag_inverts_it():
     y = mo.srs(x, perm)
     np.testing.assert_array_equal(y, mo.f64(x[0])[perm])
     np.testing.assert_array_equal(mo.sag(x[0][perm], perm), x[0])
+
+
+# ---------------------------------------------------------------- co-scheduling
+
+def test_lut_from_counts_hand_example():
+    D = np.array([[0, 3, 3], [5, 1, 0], [0, 0, 0], [0, 0, 7], [2, 2, 2]])
+    # ties go to the lower group; an unseen ID (row 2) maps to 2 mod 3
+    np.testing.assert_array_equal(mo.lut_from_counts(D), [1, 0, 2, 2, 0])
+
+
+def _brute_balanced(score):
+    n, P = score.shape
+    cap = n // P
+    best = None
+    for labels in itertools.product(range(P), repeat=n):
+        if any(labels.count(g) != cap for g in range(P)):
+            continue
+        v = sum(score[i, labels[i]] for i in range(n))
+        best = v if best is None or v > best else best
+    return best
+
+
+@pytest.mark.parametrize("seed,n,P", [(0, 6, 2), (1, 6, 3), (2, 8, 4), (3, 8, 2), (4, 4, 4)])
+def test_balanced_assign_is_optimal_and_balanced(seed, n, P):
+    rng = np.random.default_rng(seed)
+    score = rng.integers(0, 20, size=(n, P))
+    g = mo.balanced_assign(score)
+    assert (np.bincount(g, minlength=P) == n // P).all()
+    assert sum(score[i, g[i]] for i in range(n)) == _brute_balanced(score)
+
+
+def test_affinity_counts_brute_force():
+    rng = np.random.default_rng(5)
+    T, E, P, V = 9, 6, 3, 7
+    k_tok = rng.integers(0, 3, T)
+    rp = mo.row_ptr_of(k_tok)
+    ex = np.concatenate([rng.permutation(E)[:k] for k in k_tok]).astype(np.int32)
+    tok = rng.integers(0, V, T)
+    group = np.array([2, 0, 1, 1, 0, 2])
+    lut = rng.integers(0, P, V)
+    D = np.zeros((V, P), int)
+    C = np.zeros((P, E), int)
+    loc = 0
+    for t in range(T):
+        for a in range(rp[t], rp[t + 1]):
+            D[tok[t], group[ex[a]]] += 1
+            C[lut[tok[t]], ex[a]] += 1
+            loc += int(lut[tok[t]] == group[ex[a]])
+    np.testing.assert_array_equal(mo.token_group_counts(rp, ex, tok, group, V, P), D)
+    np.testing.assert_array_equal(mo.expert_group_counts(rp, ex, tok, lut, E, P), C)
+    assert mo.local_count(rp, ex, tok, group, lut) == loc
+
+
+def _planted(seed, T, E, P, V, k):
+    """Tokens of ID v only use experts of cluster v mod P (a hidden partition)."""
+    rng = np.random.default_rng(seed)
+    ecl = rng.permutation(np.repeat(np.arange(P), E // P))
+    tok = rng.integers(0, V, T)
+    sel = np.stack([rng.choice(np.nonzero(ecl == tok[t] % P)[0], k, replace=False) for t in range(T)])
+    return np.arange(0, T * k + 1, k), sel.reshape(-1).astype(np.int32), tok, rng
+
+
+@pytest.mark.parametrize("seed,E,P", [(0, 16, 4), (1, 32, 8), (2, 8, 2)])
+def test_optimize_placement_recovers_a_planted_partition(seed, E, P):
+    rp, ex, tok, rng = _planted(seed, 3000, E, P, 400, 2)
+    g0 = rng.permutation(np.repeat(np.arange(P), E // P))
+    g, lut, trace = mo.optimize_placement(rp, ex, tok, g0, 400, E, P)
+    assert (np.bincount(g, minlength=P) == E // P).all()
+    assert all(b >= a for a, b in zip(trace, trace[1:]))        # alternating ascent
+    assert mo.local_count(rp, ex, tok, g, lut) == len(ex)          # every assignment local
+    # the groups found are the hidden clusters up to relabelling
+    ecl = np.zeros(E, int)
+    for v in range(P):
+        used = np.unique(ex[np.repeat(tok % P == v, 2)])
+        ecl[used] = v
+    for grp in range(P):
+        assert len(np.unique(ecl[g == grp])) == 1
+
+
+def test_placement_of_groups_hand_example():
+    # experts 0..5 in groups [1, 0, 1, 0, 2, 2]: group 0 gets slots 0,1 (experts 1, 3)
+    np.testing.assert_array_equal(mo.placement_of_groups([1, 0, 1, 0, 2, 2], 3), [2, 0, 3, 1, 4, 5])
+
+
+def test_request_scheduling_brute_force_and_planted():
+    rng = np.random.default_rng(8)
+    V, P = 10, 3
+    lut = rng.integers(0, P, V)
+    lens = rng.integers(1, 6, 6)
+    req_ptr = np.concatenate([[0], np.cumsum(lens)])
+    tok = rng.integers(0, V, req_ptr[-1])
+    H = np.zeros((6, P), int)
+    for r in range(6):
+        for t in range(req_ptr[r], req_ptr[r + 1]):
+            H[r, lut[tok[t]]] += 1
+    np.testing.assert_array_equal(mo.request_group_hist(req_ptr, tok, lut, P), H)
+    a = mo.assign_requests(H)
+    assert (np.bincount(a, minlength=P) == 2).all()
+    assert sum(H[r, a[r]] for r in range(6)) == _brute_balanced(H)
+    # planted: each request's tokens all predicted for one group, two per group
+    lut = np.arange(V) % P
+    want = np.array([0, 1, 2, 2, 1, 0])
+    tok = np.concatenate([rng.choice(np.nonzero(lut == want[r])[0], 4) for r in range(6)])
+    req_ptr = np.arange(0, 25, 4)
+    a = mo.assign_requests(mo.request_group_hist(req_ptr, tok, lut, P))
+    np.testing.assert_array_equal(a, want)
