@@ -258,6 +258,66 @@ int32_t moe_srs(const moe_cfg* cfg, int32_t n_part, const void* x_part, const in
 int32_t moe_sag(const moe_cfg* cfg, const void* y, const int32_t* tok_perm, void* out,
                 void* stream);
 
+/*
+ * Offline co-scheduling of experts, tokens and requests (Semantic
+ * Parallelism: expert placement and token/request scheduling co-clustered
+ * as a 0-1 program solved by alternating optimisation, de technical summary
+ * §2B and key contribution 4, ko technical summary §2.2; placement fixed
+ * before deployment, ja technical overview §2.2A).  Objective: profiled
+ * assignments whose token is predicted for the group holding its expert.
+ * Experts are ORIGINAL ids (profile with the identity placement).  Profiled
+ * routing is CSR: row_ptr[n_tok+1], expert[row_ptr[n_tok]], tok[n_tok];
+ * entries out of range are ignored.  All calls: MOE_EINVAL on null
+ * pointers / bad sizes, configuration errors as moe_validate, MOE_EHIP on
+ * launch failures.
+ */
+
+/* Token step counts: counts[v*P + g] = assignments of token ID v on experts
+ * e with group[e] = g (counts [V*P] int32, device, overwritten). */
+int32_t moe_token_group_counts(const moe_cfg* cfg, int32_t n_tok, const int32_t* row_ptr,
+                               const int32_t* expert, const int32_t* tok, const int32_t* group,
+                               int32_t* counts, void* stream);
+
+/* Token step: lut[v] = argmax_g counts[v*P + g], ties to the lower group,
+ * IDs with no count map to v mod P (lut [V] int32, device). */
+int32_t moe_lut_from_counts(const moe_cfg* cfg, const int32_t* counts, int32_t* lut, void* stream);
+
+/* Expert step counts: counts[g*E + e] = assignments at expert e of tokens
+ * with lut[tok] = g (counts [P*E] int32, device, overwritten). */
+int32_t moe_expert_group_counts(const moe_cfg* cfg, int32_t n_tok, const int32_t* row_ptr,
+                                const int32_t* expert, const int32_t* tok, const int32_t* lut,
+                                int32_t* counts, void* stream);
+
+/* Host only.  Assigns n items to P groups, n/P per group, maximising
+ * sum_i score[i*P + group[i]] exactly (Hungarian method, O(n^3), n <= 4096).
+ * score [n*P] and group [n] are host arrays.  Returns the optimum, or a
+ * negative moe_status (MOE_ESHAPE unless P divides n, MOE_EINVAL on NULL). */
+int64_t moe_balanced_assign(int32_t n, int32_t P, const int64_t* score, int32_t* group);
+
+/* Alternating optimisation of the expert grouping, starting from the
+ * balanced grouping group[E] (host, in/out): token step (lut), then expert
+ * step (moe_balanced_assign on the expert counts); stops after max_iters
+ * rounds or when the expert step gains nothing (the grouping is then kept).
+ * Outputs: group (host), perm[E] (host, slot of each original expert: group
+ * g's experts take slots [g*E/P, (g+1)*E/P) in ascending id; or NULL),
+ * lut[V] (device, the token step of the final grouping), objective
+ * [2*max_iters] (host or NULL: the objective before and after each expert
+ * step), n_steps (host or NULL: entries written).  counts_vp [V*P] and
+ * counts_pe [P*E] are device scratch.  SYNCHRONOUS: waits on `stream`. */
+int32_t moe_optimize_placement(const moe_cfg* cfg, int32_t n_tok, const int32_t* row_ptr,
+                               const int32_t* expert, const int32_t* tok, int32_t max_iters,
+                               int32_t* group, int32_t* perm, int32_t* lut, int32_t* counts_vp,
+                               int32_t* counts_pe, int64_t* objective, int32_t* n_steps,
+                               void* stream);
+
+/* Inter-request scheduling under attention data parallelism (de technical
+ * summary §2B; ko technical summary §2.2): hist[r*P + g] = tokens of request
+ * r (tokens [req_ptr[r], req_ptr[r+1]) of tok) with lut[tok] = g (device,
+ * int32, P <= 64).  Requests then go to ranks with moe_balanced_assign on
+ * hist. */
+int32_t moe_request_group_hist(const moe_cfg* cfg, int32_t n_req, const int32_t* req_ptr,
+                               const int32_t* tok, const int32_t* lut, int32_t* hist, void* stream);
+
 /* Device tensors of one layer for moe_forward (host struct of device pointers). */
 typedef struct moe_weights {
     const void* Wg;              /* [E,H] slot order */

@@ -23,13 +23,15 @@ def m():
 def declared_functions():
     src = open(os.path.join(ROOT, "include", "moe.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:int32_t|size_t|const char\*)\s+(moe_\w+)\s*\(", src, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:int32_t|int64_t|size_t|const char\*)\s+(moe_\w+)\s*\(", src, re.M)))
 
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "moe_combine", "moe_expert_ffn", "moe_forward", "moe_last_error", "moe_route",
-        "moe_sag", "moe_shuffle", "moe_srs", "moe_validate", "moe_workspace_bytes"])
+        "moe_sag", "moe_shuffle", "moe_srs", "moe_validate", "moe_workspace_bytes",
+        "moe_token_group_counts", "moe_lut_from_counts", "moe_expert_group_counts",
+        "moe_balanced_assign", "moe_optimize_placement", "moe_request_group_hist"])
 
 
 def test_library_exports_every_declared_symbol(m):
@@ -185,3 +187,38 @@ def test_srs_sag_reject_bad_arguments_before_launching(m):
     empty = _cfgs(m)["dsv2lite"]
     empty.T = 0                          # nothing to do, nothing touched
     assert m.lib().moe_srs(ctypes.byref(empty), 8, None, None, None, None) == m.MOE_OK
+
+
+def test_balanced_assign_host_only(m):
+    """The host-only solver runs without a GPU; checked against brute force
+    (the same rule the oracle's pin uses, independently of the oracle)."""
+    import itertools
+    import numpy as np
+    rng = np.random.default_rng(4)
+    for n, P in [(6, 2), (6, 3), (8, 4), (4, 1), (0, 2)]:
+        score = rng.integers(0, 50, size=(n, P))
+        g, best = m.moe_balanced_assign(score)
+        assert (np.bincount(g, minlength=P) == n // P).all()
+        assert best == sum(score[i, g[i]] for i in range(n))
+        brute = max([sum(score[i, lab[i]] for i in range(n))
+                     for lab in itertools.product(range(P), repeat=n)
+                     if all(lab.count(q) == n // P for q in range(P))] or [0])
+        assert best == brute
+    assert m.lib().moe_balanced_assign(5, 2, None, None) == m.MOE_ESHAPE
+
+
+def test_coscheduling_calls_reject_bad_arguments(m):
+    c = _cfgs(m)["dsv2lite"]
+    fake = ctypes.c_void_p(0x1000)
+    lib = m.lib()
+    assert lib.moe_token_group_counts(ctypes.byref(c), -1, fake, fake, fake, fake, fake, None) == m.MOE_EINVAL
+    assert lib.moe_token_group_counts(ctypes.byref(c), 4, None, fake, fake, fake, fake, None) == m.MOE_EINVAL
+    assert lib.moe_expert_group_counts(ctypes.byref(c), 4, fake, fake, fake, None, fake, None) == m.MOE_EINVAL
+    assert lib.moe_lut_from_counts(ctypes.byref(c), None, fake, None) == m.MOE_EINVAL
+    assert lib.moe_request_group_hist(ctypes.byref(c), 3, fake, fake, fake, None, None) == m.MOE_EINVAL
+    import numpy as np
+    group = np.zeros(c.E, np.int32)             # not balanced: every expert in group 0
+    rc = lib.moe_optimize_placement(ctypes.byref(c), 4, fake, fake, fake, 5,
+                                    group.ctypes.data_as(ctypes.c_void_p), None, fake, fake, fake,
+                                    None, None, None)
+    assert rc == m.MOE_EINVAL

@@ -1,0 +1,144 @@
+"""GPU parity of the offline co-scheduling calls against the oracle: the two
+count kernels and the token table bit for bit, the balanced assignment's
+optimum, the alternating optimisation's first round exactly and its result
+as a valid, monotone ascent; request histograms bit for bit.  Profiled
+routing comes from the oracle (never from the HIP path)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as mo
+from tests import harness as hn
+from token_routing_shuffle_amd import workload as wl
+
+pytestmark = pytest.mark.gpu
+
+
+def moe_mod():
+    from token_routing_shuffle_amd import moe
+    return moe
+
+
+def oracle_profile(cfg, n):
+    """Oracle routing (original expert ids, CSR) of an n-token profiling draw."""
+    tb = wl.make_tables(cfg, profile_tokens=n)
+    xh = hn.host(wl.make_prof_x(cfg, "cpu", n=n))
+    Wg = hn.host(wl.make_gate(cfg, "cpu"))
+    tok = tb.prof_tok[:n]
+    l64 = mo.logits(xh, Wg, tok, tb.pref, cfg.aff_bias if tb.pref is not None else 0.0)
+    sel, _ = mo.route(l64, cfg, None, tb.ebias)
+    kt = (sel >= 0).sum(axis=1)
+    rp = mo.row_ptr_of(kt)
+    ex = sel[sel >= 0].astype(np.int32)
+    return tb, rp, ex, tok.astype(np.int32)
+
+
+@pytest.fixture(scope="module")
+def prof():
+    cfg = wl.CONFIGS["dsv2lite"]
+    tb, rp, ex, tok = oracle_profile(cfg, 4096)
+    return cfg, tb, rp, ex, tok
+
+
+def test_count_kernels_and_token_table(prof):
+    m = moe_mod()
+    cfg, tb, rp, ex, tok = prof
+    c = m.make_cfg(cfg)
+    E, P, V = cfg.E, cfg.P, cfg.V
+    n = len(tok)
+    group = (tb.perm // (E // P)).astype(np.int32)
+    d = {k: hn.to_dev(v) for k, v in dict(rp=rp.astype(np.int32), ex=ex, tok=tok, group=group).items()}
+    D = torch.empty(V * P, dtype=torch.int32, device=hn.DEV)
+    lut = torch.empty(V, dtype=torch.int32, device=hn.DEV)
+    C = torch.empty(P * E, dtype=torch.int32, device=hn.DEV)
+    m.moe_token_group_counts(c, n, d["rp"], d["ex"], d["tok"], d["group"], D)
+    m.moe_lut_from_counts(c, D, lut)
+    torch.cuda.synchronize()
+    D_or = mo.token_group_counts(rp, ex, tok, group, V, P)
+    np.testing.assert_array_equal(hn.host(D).reshape(V, P), D_or)
+    lut_or = mo.lut_from_counts(D_or)
+    np.testing.assert_array_equal(hn.host(lut), lut_or)
+    m.moe_expert_group_counts(c, n, d["rp"], d["ex"], d["tok"], hn.to_dev(lut_or), C)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(hn.host(C).reshape(P, E), mo.expert_group_counts(rp, ex, tok, lut_or, E, P))
+
+
+def test_optimize_placement_against_oracle(prof):
+    m = moe_mod()
+    cfg, tb, rp, ex, tok = prof
+    c = m.make_cfg(cfg)
+    E, P, V = cfg.E, cfg.P, cfg.V
+    group0 = (tb.perm // (E // P)).astype(np.int32)
+    lut = torch.empty(V, dtype=torch.int32, device=hn.DEV)
+    g, perm, trace = m.moe_optimize_placement(
+        c, len(tok), hn.to_dev(rp.astype(np.int32)), hn.to_dev(ex), hn.to_dev(tok), group0, lut,
+        torch.empty(V * P, dtype=torch.int32, device=hn.DEV),
+        torch.empty(P * E, dtype=torch.int32, device=hn.DEV), max_iters=10)
+    g_or, lut_or, trace_or = mo.optimize_placement(rp, ex, tok, group0, V, E, P, max_iters=10)
+    print("[cosched] trace gpu", trace.tolist(), "oracle", trace_or, flush=True)
+    # first round: same start, so the same counts and the same optimum value
+    assert trace[0] == trace_or[0] and trace[1] == trace_or[1]
+    assert all(b >= a for a, b in zip(trace, trace[1:]))
+    assert (np.bincount(g, minlength=P) == E // P).all()
+    np.testing.assert_array_equal(perm, mo.placement_of_groups(g, P))
+    lut_h = hn.host(lut)
+    np.testing.assert_array_equal(lut_h, mo.lut_from_counts(mo.token_group_counts(rp, ex, tok, g, V, P)))
+    final = mo.local_count(rp, ex, tok, g, lut_h)
+    assert final >= max(trace[-2:])
+    assert final >= trace_or[1]
+    # held-out draw: the layer's own tokens, routed by the oracle
+    cfg_h = cfg.replace(T=2048)
+    tbh = wl.make_tables(cfg_h, profile_tokens=16)
+    xh = hn.host(wl.make_x(cfg_h, "cpu"))
+    Wg = hn.host(wl.make_gate(cfg_h, "cpu"))
+    l64 = mo.logits(xh, Wg, tbh.tok, tbh.pref, cfg.aff_bias)
+    sel, _ = mo.route(l64, cfg_h, None, tbh.ebias)
+    rph = mo.row_ptr_of((sel >= 0).sum(axis=1))
+    exh = sel[sel >= 0]
+    lar0 = mo.local_count(rph, exh, tbh.tok, group0, mo.lut_from_counts(
+        mo.token_group_counts(rp, ex, tok, group0, V, P))) / len(exh)
+    lar1 = mo.local_count(rph, exh, tbh.tok, g, lut_h) / len(exh)
+    print("[cosched] held-out LAR random %.3f -> optimised %.3f" % (lar0, lar1), flush=True)
+    assert lar1 > lar0
+
+
+def test_optimize_placement_recovers_planted_partition():
+    m = moe_mod()
+    rng = np.random.default_rng(0)
+    E, P, V, T, k = 32, 8, 400, 3000, 2
+    cfg = wl.CONFIGS["dsv2lite"].replace(E=E, P=P, V=V, k=k, T=T)
+    c = m.make_cfg(cfg)
+    ecl = rng.permutation(np.repeat(np.arange(P), E // P))
+    tok = rng.integers(0, V, T).astype(np.int32)
+    sel = np.stack([rng.choice(np.nonzero(ecl == tok[t] % P)[0], k, replace=False) for t in range(T)])
+    rp = np.arange(0, T * k + 1, k).astype(np.int32)
+    ex = sel.reshape(-1).astype(np.int32)
+    g0 = rng.permutation(np.repeat(np.arange(P), E // P)).astype(np.int32)
+    lut = torch.empty(V, dtype=torch.int32, device=hn.DEV)
+    g, perm, trace = m.moe_optimize_placement(
+        c, T, hn.to_dev(rp), hn.to_dev(ex), hn.to_dev(tok), g0, lut,
+        torch.empty(V * P, dtype=torch.int32, device=hn.DEV),
+        torch.empty(P * E, dtype=torch.int32, device=hn.DEV))
+    assert mo.local_count(rp, ex, tok, g, hn.host(lut)) == T * k
+
+
+def test_request_histograms_and_assignment():
+    m = moe_mod()
+    cfg = wl.CONFIGS["prism"]
+    c = m.make_cfg(cfg)
+    tb = wl.make_tables(cfg, profile_tokens=16)
+    rng = np.random.default_rng(2)
+    lut = rng.integers(0, cfg.P, cfg.V).astype(np.int32)
+    req_ptr = np.arange(0, cfg.T + 1, cfg.req_tokens).astype(np.int32)
+    R = len(req_ptr) - 1
+    H = torch.empty(R * cfg.P, dtype=torch.int32, device=hn.DEV)
+    m.moe_request_group_hist(c, R, hn.to_dev(req_ptr), hn.to_dev(tb.tok.astype(np.int32)),
+                             hn.to_dev(lut), H)
+    torch.cuda.synchronize()
+    H_or = mo.request_group_hist(req_ptr, tb.tok, lut, cfg.P)
+    Hh = hn.host(H).reshape(R, cfg.P)
+    np.testing.assert_array_equal(Hh, H_or)
+    a, best = m.moe_balanced_assign(Hh)
+    a_or = mo.assign_requests(H_or)
+    assert best == sum(H_or[r, a_or[r]] for r in range(R))
+    assert (np.bincount(a, minlength=cfg.P) == R // cfg.P).all()

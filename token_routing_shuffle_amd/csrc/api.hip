@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <vector>
 
 #include "internal.h"
 
@@ -379,6 +380,166 @@ MOE_API int32_t moe_sag(const moe_cfg* cfg, const void* y, const int32_t* tok_pe
     if (y == out) return fail(MOE_EINVAL, "y and out must not overlap");
     hipError_t e = launch_sag(c, y, tok_perm, out, (hipStream_t)stream);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_sag");
+}
+
+// ---------------------------------------------------------------- co-scheduling
+
+MOE_API int32_t moe_token_group_counts(const moe_cfg* cfg, int32_t n_tok, const int32_t* row_ptr,
+                                       const int32_t* expert, const int32_t* tok,
+                                       const int32_t* group, int32_t* counts, void* stream)
+{
+    int32_t rc = check_cfg(cfg);
+    if (rc != MOE_OK) return rc;
+    const moe_cfg& c = *cfg;
+    if (n_tok < 0) return fail(MOE_EINVAL, "n_tok < 0");
+    REQUIRE(counts);
+    if (n_tok > 0) {
+        REQUIRE(row_ptr);
+        REQUIRE(expert);
+        REQUIRE(tok);
+        REQUIRE(group);
+    }
+    hipError_t e = launch_token_group_counts(n_tok, c.V, c.E, c.P, row_ptr, expert, tok, group, counts,
+                                             (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_token_group_counts");
+}
+
+MOE_API int32_t moe_lut_from_counts(const moe_cfg* cfg, const int32_t* counts, int32_t* lut,
+                                    void* stream)
+{
+    int32_t rc = check_cfg(cfg);
+    if (rc != MOE_OK) return rc;
+    REQUIRE(counts);
+    REQUIRE(lut);
+    hipError_t e = launch_lut_from_counts(cfg->V, cfg->P, counts, lut, (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_lut_from_counts");
+}
+
+MOE_API int32_t moe_expert_group_counts(const moe_cfg* cfg, int32_t n_tok, const int32_t* row_ptr,
+                                        const int32_t* expert, const int32_t* tok,
+                                        const int32_t* lut, int32_t* counts, void* stream)
+{
+    int32_t rc = check_cfg(cfg);
+    if (rc != MOE_OK) return rc;
+    const moe_cfg& c = *cfg;
+    if (n_tok < 0) return fail(MOE_EINVAL, "n_tok < 0");
+    REQUIRE(counts);
+    if (n_tok > 0) {
+        REQUIRE(row_ptr);
+        REQUIRE(expert);
+        REQUIRE(tok);
+        REQUIRE(lut);
+    }
+    hipError_t e = launch_expert_group_counts(n_tok, c.V, c.E, c.P, row_ptr, expert, tok, lut, counts,
+                                              (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_expert_group_counts");
+}
+
+MOE_API int64_t moe_balanced_assign(int32_t n, int32_t P, const int64_t* score, int32_t* group)
+{
+    if (n < 0 || P < 1 || n % P != 0) return fail(MOE_ESHAPE, "need n >= 0, P >= 1, P | n");
+    if (n > 4096) return fail(MOE_ESHAPE, "n > 4096");
+    if (n > 0) {
+        REQUIRE(score);
+        REQUIRE(group);
+    }
+    return balanced_assign_host(n, P, (const long long*)score, group);
+}
+
+MOE_API int32_t moe_optimize_placement(const moe_cfg* cfg, int32_t n_tok, const int32_t* row_ptr,
+                                       const int32_t* expert, const int32_t* tok, int32_t max_iters,
+                                       int32_t* group, int32_t* perm, int32_t* lut,
+                                       int32_t* counts_vp, int32_t* counts_pe, int64_t* objective,
+                                       int32_t* n_steps, void* stream)
+{
+    int32_t rc = check_cfg(cfg);
+    if (rc != MOE_OK) return rc;
+    const moe_cfg& c = *cfg;
+    const int E = c.E, P = c.P, epg = c.E / c.P;
+    if (n_tok < 0 || max_iters < 1) return fail(MOE_EINVAL, "n_tok < 0 or max_iters < 1");
+    REQUIRE(group);
+    REQUIRE(lut);
+    REQUIRE(counts_vp);
+    REQUIRE(counts_pe);
+    if (n_tok > 0) {
+        REQUIRE(row_ptr);
+        REQUIRE(expert);
+        REQUIRE(tok);
+    }
+    std::vector<int> cnt(P, 0);
+    for (int e = 0; e < E; ++e) {
+        if (group[e] < 0 || group[e] >= P) return fail(MOE_EINVAL, "group[%d] out of range", e);
+        ++cnt[group[e]];
+    }
+    for (int g = 0; g < P; ++g)
+        if (cnt[g] != epg) return fail(MOE_EINVAL, "initial grouping is not balanced");
+    hipStream_t s = (hipStream_t)stream;
+    int32_t* dgroup = counts_pe;   // the expert grouping rides in the first E ints of counts_pe
+    std::vector<int32_t> hC((size_t)P * E), cur(group, group + E), nxt(E);
+    std::vector<long long> score((size_t)E * P);
+    int steps = 0;
+    hipError_t e = hipSuccess;
+#define HIPCHK(x)                                           \
+    do {                                                    \
+        e = (x);                                            \
+        if (e != hipSuccess) return hip_fail(e, "moe_optimize_placement"); \
+    } while (0)
+    // token step for the grouping `cur`: lut on the device
+    auto token_step = [&]() -> hipError_t {
+        hipError_t r = hipMemcpyAsync(dgroup, cur.data(), E * sizeof(int32_t), hipMemcpyHostToDevice, s);
+        if (r != hipSuccess) return r;
+        r = launch_token_group_counts(n_tok, c.V, E, P, row_ptr, expert, tok, dgroup, counts_vp, s);
+        if (r != hipSuccess) return r;
+        return launch_lut_from_counts(c.V, P, counts_vp, lut, s);
+    };
+    for (int it = 0; it < max_iters; ++it) {
+        HIPCHK(token_step());
+        HIPCHK(launch_expert_group_counts(n_tok, c.V, E, P, row_ptr, expert, tok, lut, counts_pe, s));
+        HIPCHK(hipMemcpyAsync(hC.data(), counts_pe, hC.size() * sizeof(int32_t), hipMemcpyDeviceToHost, s));
+        HIPCHK(hipStreamSynchronize(s));
+        long long before = 0;
+        for (int x = 0; x < E; ++x) {
+            before += hC[(size_t)cur[x] * E + x];
+            for (int g = 0; g < P; ++g) score[(size_t)x * P + g] = hC[(size_t)g * E + x];
+        }
+        const long long after = balanced_assign_host(E, P, score.data(), nxt.data());
+        if (objective) {
+            objective[2 * it] = before;
+            objective[2 * it + 1] = after;
+        }
+        steps = 2 * it + 2;
+        if (after <= before) break;   // no strict gain: keep the current grouping
+        cur = nxt;
+    }
+    HIPCHK(token_step());             // final table for the kept grouping
+    HIPCHK(hipStreamSynchronize(s));
+#undef HIPCHK
+    std::copy(cur.begin(), cur.end(), group);
+    if (perm) {
+        // group g's experts take slots [g*E/P, (g+1)*E/P) in ascending id
+        std::vector<int> next_slot(P);
+        for (int g = 0; g < P; ++g) next_slot[g] = g * epg;
+        for (int x = 0; x < E; ++x) perm[x] = next_slot[cur[x]]++;
+    }
+    if (n_steps) *n_steps = steps;
+    return MOE_OK;
+}
+
+MOE_API int32_t moe_request_group_hist(const moe_cfg* cfg, int32_t n_req, const int32_t* req_ptr,
+                                       const int32_t* tok, const int32_t* lut, int32_t* hist,
+                                       void* stream)
+{
+    int32_t rc = check_cfg(cfg);
+    if (rc != MOE_OK) return rc;
+    if (n_req < 0) return fail(MOE_EINVAL, "n_req < 0");
+    if (n_req == 0) return MOE_OK;
+    REQUIRE(req_ptr);
+    REQUIRE(tok);
+    REQUIRE(lut);
+    REQUIRE(hist);
+    hipError_t e = launch_request_group_hist(n_req, cfg->V, cfg->P, req_ptr, tok, lut, hist,
+                                             (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_request_group_hist");
 }
 
 MOE_API int32_t moe_forward(const moe_cfg* cfg, const moe_weights* w, const moe_inputs* in,

@@ -89,4 +89,18 @@ hipError_t launch_srs(const moe_cfg& c, int n_part, const void* x_part, const in
 hipError_t launch_sag(const moe_cfg& c, const void* y, const int32_t* tok_perm, void* out,
                       hipStream_t s);
 
+// offline co-scheduling (cosched.hip)
+hipError_t launch_fill_i32(int32_t* p, long long n, int32_t v, hipStream_t s);
+hipError_t launch_token_group_counts(int n_tok, int V, int E, int P, const int32_t* row_ptr,
+                                     const int32_t* expert, const int32_t* tok, const int32_t* group,
+                                     int32_t* D, hipStream_t s);
+hipError_t launch_lut_from_counts(int V, int P, const int32_t* D, int32_t* lut, hipStream_t s);
+hipError_t launch_expert_group_counts(int n_tok, int V, int E, int P, const int32_t* row_ptr,
+                                      const int32_t* expert, const int32_t* tok, const int32_t* lut,
+                                      int32_t* C, hipStream_t s);
+hipError_t launch_request_group_hist(int n_req, int V, int P, const int32_t* req_ptr,
+                                     const int32_t* tok, const int32_t* lut, int32_t* H,
+                                     hipStream_t s);
+long long balanced_assign_host(int n, int P, const long long* score, int32_t* group);
+
 }  // namespace moe

@@ -90,6 +90,19 @@ def _load():
     lib.moe_srs.argtypes = [P(moe_cfg), i32, vp, vp, vp, vp]
     lib.moe_sag.restype = i32
     lib.moe_sag.argtypes = [P(moe_cfg), vp, vp, vp, vp]
+    lib.moe_token_group_counts.restype = i32
+    lib.moe_token_group_counts.argtypes = [P(moe_cfg), i32, vp, vp, vp, vp, vp, vp]
+    lib.moe_lut_from_counts.restype = i32
+    lib.moe_lut_from_counts.argtypes = [P(moe_cfg), vp, vp, vp]
+    lib.moe_expert_group_counts.restype = i32
+    lib.moe_expert_group_counts.argtypes = [P(moe_cfg), i32, vp, vp, vp, vp, vp, vp]
+    lib.moe_balanced_assign.restype = ctypes.c_int64
+    lib.moe_balanced_assign.argtypes = [i32, i32, vp, vp]
+    lib.moe_optimize_placement.restype = i32
+    lib.moe_optimize_placement.argtypes = [P(moe_cfg), i32, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp,
+                                           vp, vp]
+    lib.moe_request_group_hist.restype = i32
+    lib.moe_request_group_hist.argtypes = [P(moe_cfg), i32, vp, vp, vp, vp, vp]
     lib.moe_forward.restype = i32
     lib.moe_forward.argtypes = [P(moe_cfg), P(moe_weights), P(moe_inputs), vp, P(moe_exports),
                                 vp, sz, vp]
@@ -107,7 +120,9 @@ def lib():
 
 
 EXPORTED = ("moe_validate", "moe_workspace_bytes", "moe_last_error", "moe_route", "moe_shuffle",
-            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_srs", "moe_sag")
+            "moe_expert_ffn", "moe_combine", "moe_forward", "moe_srs", "moe_sag",
+            "moe_token_group_counts", "moe_lut_from_counts", "moe_expert_group_counts",
+            "moe_balanced_assign", "moe_optimize_placement", "moe_request_group_hist")
 
 
 def _p(t) -> Optional[int]:
@@ -216,6 +231,62 @@ def moe_srs(cfg, n_part, x_part, tok_perm, y, stream=None):
 def moe_sag(cfg, y, tok_perm, out, stream=None):
     rc = lib().moe_sag(ctypes.byref(cfg), _p(y), _p(tok_perm), _p(out), _stream(stream))
     _check(rc, "moe_sag")
+
+
+def _host_ptr(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def moe_token_group_counts(cfg, n_tok, row_ptr, expert, tok, group, counts, stream=None):
+    rc = lib().moe_token_group_counts(ctypes.byref(cfg), int(n_tok), _p(row_ptr), _p(expert), _p(tok),
+                                      _p(group), _p(counts), _stream(stream))
+    _check(rc, "moe_token_group_counts")
+
+
+def moe_lut_from_counts(cfg, counts, lut, stream=None):
+    rc = lib().moe_lut_from_counts(ctypes.byref(cfg), _p(counts), _p(lut), _stream(stream))
+    _check(rc, "moe_lut_from_counts")
+
+
+def moe_expert_group_counts(cfg, n_tok, row_ptr, expert, tok, lut, counts, stream=None):
+    rc = lib().moe_expert_group_counts(ctypes.byref(cfg), int(n_tok), _p(row_ptr), _p(expert),
+                                       _p(tok), _p(lut), _p(counts), _stream(stream))
+    _check(rc, "moe_expert_group_counts")
+
+
+def moe_balanced_assign(score):
+    """score: host int64 array [n, P]; returns (group int32 [n], optimum)."""
+    import numpy as np
+    score = np.ascontiguousarray(score, dtype=np.int64)
+    n, P = score.shape
+    group = np.zeros(n, np.int32)
+    best = lib().moe_balanced_assign(n, P, _host_ptr(score), _host_ptr(group))
+    if best < 0:
+        _check(int(best), "moe_balanced_assign")
+    return group, int(best)
+
+
+def moe_optimize_placement(cfg, n_tok, row_ptr, expert, tok, group0, lut, counts_vp, counts_pe,
+                           max_iters=20, stream=None):
+    """Returns (group, perm, objective trace) as host arrays; lut (device) is
+    filled with the final token table."""
+    import numpy as np
+    group = np.ascontiguousarray(group0, dtype=np.int32).copy()
+    perm = np.zeros_like(group)
+    obj = np.zeros(2 * max_iters, np.int64)
+    n_steps = ctypes.c_int32(0)
+    rc = lib().moe_optimize_placement(ctypes.byref(cfg), int(n_tok), _p(row_ptr), _p(expert), _p(tok),
+                                      int(max_iters), _host_ptr(group), _host_ptr(perm), _p(lut),
+                                      _p(counts_vp), _p(counts_pe), _host_ptr(obj),
+                                      ctypes.byref(n_steps), _stream(stream))
+    _check(rc, "moe_optimize_placement")
+    return group, perm, obj[:n_steps.value]
+
+
+def moe_request_group_hist(cfg, n_req, req_ptr, tok, lut, hist, stream=None):
+    rc = lib().moe_request_group_hist(ctypes.byref(cfg), int(n_req), _p(req_ptr), _p(tok), _p(lut),
+                                      _p(hist), _stream(stream))
+    _check(rc, "moe_request_group_hist")
 
 
 def moe_forward(cfg, weights: moe_weights, inputs: moe_inputs, out, exports=None, ws=None,

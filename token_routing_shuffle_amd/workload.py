@@ -225,6 +225,13 @@ def make_x(cfg: LayerConfig, device="cpu", n: Optional[int] = None, stream="x"):
     return x[:n].contiguous() if x.shape[0] != n else x
 
 
+def make_gate(cfg: LayerConfig, device="cpu"):
+    """The gate rows Wg[E, H] alone, as make_weights draws them on `device`
+    (the draw depends on the device's generator)."""
+    st = _streams(cfg)
+    return _randn((cfg.E, cfg.H), cfg.H ** -0.5, _gen(st["Wg"], device), device, cfg.dtype)
+
+
 def make_partials(cfg: LayerConfig, n_part: int, device="cpu", n: Optional[int] = None):
     """Tensor-parallel partial sums x_part[n_part, n, H] of an attention
     output, each ~ N(0, 1/n_part) so that their sum is ~ N(0, 1)
