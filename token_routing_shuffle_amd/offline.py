@@ -44,15 +44,15 @@ def device_layer(cfg, tables, w: dict, lut: np.ndarray, device="cuda") -> dict:
     return d
 
 
-def profile_lut(cfg, dev: dict, prof_x: torch.Tensor, prof_tok: np.ndarray,
-                chunk: int = 16384) -> np.ndarray:
-    """Token->group table from routing a profiling draw with moe_route."""
+def profile_routing(cfg, dev: dict, prof_x: torch.Tensor, prof_tok: np.ndarray,
+                    chunk: int = 16384):
+    """Route a profiling draw with moe_route (chunks of `chunk` tokens) and
+    return the whole draw's routing as device CSR (row_ptr [n+1], slots [A])
+    plus its token IDs (device int32)."""
     device = prof_x.device
     n = prof_x.shape[0]
-    E, P = cfg.E, cfg.P
-    epg = E // P
-    counts = np.zeros((cfg.V, P), np.int64)
     tok_all = torch.as_tensor(np.asarray(prof_tok, np.int32), device=device)
+    rps, sls, base = [torch.zeros(1, dtype=torch.int32, device=device)], [], 0
     for s in range(0, n, chunk):
         m = min(chunk, n - s)
         c = moe.make_cfg(cfg, T=m)
@@ -64,12 +64,31 @@ def profile_lut(cfg, dev: dict, prof_x: torch.Tensor, prof_tok: np.ndarray,
         wts = torch.empty(m * cfg.k, dtype=torch.float32, device=device)
         moe.moe_route(c, prof_x[s:s + m], dev["Wg"], dev.get("ebias"), dev["slot_to_orig"],
                       tok_all[s:s + m], dev.get("pref"), k_tok, row_ptr, slots, wts)
-        rp = row_ptr.cpu().numpy()
-        sl = slots.cpu().numpy()[: rp[-1]]
-        t_of_a = np.repeat(np.arange(m), np.diff(rp))
-        v = np.asarray(prof_tok[s:s + m])[t_of_a]
-        np.add.at(counts, (v, sl // epg), 1)
-    lut = np.argmax(counts, axis=1).astype(np.int32)
-    unseen = counts.sum(axis=1) == 0
-    lut[unseen] = (np.arange(cfg.V)[unseen] % P).astype(np.int32)
+        a = int(row_ptr[m].item())
+        rps.append(row_ptr[1:] + base)
+        sls.append(slots[:a])
+        base += a
+    return torch.cat(rps), torch.cat(sls), tok_all
+
+
+def lut_of_grouping(cfg, row_ptr, slots, tok, group: np.ndarray) -> torch.Tensor:
+    """Token step of the co-scheduling (moe_token_group_counts and
+    moe_lut_from_counts): the group that receives most of each token ID's
+    profiled assignments; group[s] = placement group of slot s."""
+    device = row_ptr.device
+    c = moe.make_cfg(cfg)
+    counts = torch.empty(cfg.V * cfg.P, dtype=torch.int32, device=device)
+    lut = torch.empty(cfg.V, dtype=torch.int32, device=device)
+    moe.moe_token_group_counts(c, tok.numel(), row_ptr, slots, tok,
+                               torch.as_tensor(np.asarray(group, np.int32), device=device), counts)
+    moe.moe_lut_from_counts(c, counts, lut)
     return lut
+
+
+def profile_lut(cfg, dev: dict, prof_x: torch.Tensor, prof_tok: np.ndarray,
+                chunk: int = 16384) -> np.ndarray:
+    """Token->group table from routing a profiling draw with moe_route, for
+    the layer's current placement (slot s is in group s // (E/P))."""
+    rp, sl, tok = profile_routing(cfg, dev, prof_x, prof_tok, chunk)
+    group = np.arange(cfg.E, dtype=np.int32) // (cfg.E // cfg.P)
+    return lut_of_grouping(cfg, rp, sl, tok, group).cpu().numpy()
