@@ -212,10 +212,16 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
             kt = p.shK / BK;
         }
     };
+    // A segment of cnt rows is cut into mt = ceil(cnt / 256) m-tiles of
+    // equal height (a multiple of 64 rows): the tiles that share a weight tile
+    // then run at the same speed, so the second reader finds it in L2.
+    auto mtile_h = [&](int cnt) {
+        const int mt = (cnt + BM - 1) / BM;
+        return ((cnt + mt - 1) / mt + 63) / 64 * 64;
+    };
     auto ntile_work = [&](int cnt, int kt) {
         const int mt = (cnt + BM - 1) / BM;
-        const int last = cnt - (mt - 1) * BM;
-        return ((mt - 1) * 4 + (last + 63) / 64) * kt;
+        return mt * (mtile_h(cnt) / 64) * kt;
     };
     {
         constexpr int SPT = (kMaxSeg + kThreads - 1) / kThreads;
@@ -274,7 +280,7 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
                 const int wn_ = ntile_work(cnt, kt);
                 const int rem = (int)(target - s_wpref[lo]);
                 const int n = rem / wn_;
-                const int m = min((rem % wn_) / (4 * kt), mt - 1);
+                const int m = min((rem % wn_) / ((mtile_h(cnt) / 64) * kt), mt - 1);
                 b = s_pref[lo] + n * mt + m;
             }
             s_bound[tid] = b;
@@ -301,10 +307,11 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
         const int cnt = __builtin_amdgcn_readfirstlane(s_cnt[seg]);
         const int mt = (cnt + BM - 1) / BM;
         const int local = L - __builtin_amdgcn_readfirstlane(s_pref[seg]);
-        const int ntile = local / mt, m0 = (local % mt) * BM;
+        const int hgt = mtile_h(cnt);
+        const int ntile = local / mt, m0 = (local % mt) * hgt;
         const int K = shared ? p.shK : p.K;
         const int N = shared ? p.shN : p.N;
-        const int rows = min(BM, cnt - m0);
+        const int rows = min(hgt, cnt - m0);
 
         // ---- operands as buffer resources (base + bounds); per-lane 32-bit
         // row offsets; the k-step goes in the scalar offset.  Rows past the
@@ -505,9 +512,9 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
                 __syncthreads();
             }
         };
-        if (rows > 192) run_tile(IntC<8>{});
-        else if (rows > 128) run_tile(IntC<6>{});
-        else if (rows > 64) run_tile(IntC<4>{});
+        if (hgt > 192) run_tile(IntC<8>{});
+        else if (hgt > 128) run_tile(IntC<6>{});
+        else if (hgt > 64) run_tile(IntC<4>{});
         else run_tile(IntC<2>{});
     }
 }
