@@ -105,7 +105,8 @@ WsLayout ws_layout(const moe_cfg& c)
     const size_t T = (size_t)c.T, A = (size_t)c.T * c.k_max, E = c.E, P = c.P;
     const size_t es = (size_t)esize(c);
     const size_t Ish = (size_t)c.n_shared * c.I_shared;
-    L.nb = std::max(1, ceil_div(c.T, kShuffleTPB));
+    L.tpb = shuffle_tpb(c.T, c.E, c.P);
+    L.nb = std::max(1, ceil_div(c.T, L.tpb));
     L.row_ptr = take((T + 1) * 4);
     L.topk_slot = take(A * 4);
     L.topk_w = take(A * 4);
@@ -254,7 +255,7 @@ MOE_API int32_t moe_shuffle(const moe_cfg* cfg, const int32_t* row_ptr, const in
     o.thist = at<int32_t>(ws, L.thist);
     o.gemm_ctr = nullptr;
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = launch_shuffle(c, L.nb, row_ptr, topk_slot, tok, lut, o, s);
+    hipError_t e = launch_shuffle(c, L.nb, L.tpb, row_ptr, topk_slot, tok, lut, o, s);
     if (e == hipSuccess && x_sorted != nullptr) e = launch_gather(c, x, row_ptr, assign_to_sorted, x_sorted, s);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_shuffle");
 }
@@ -616,7 +617,7 @@ MOE_API int32_t moe_forward(const moe_cfg* cfg, const moe_weights* w, const moe_
                       row_ptr, topk_slot, topk_w, X->logits, s));
     STEP(record(X, MOE_STAGE_ROUTE, 1, s));
     STEP(record(X, MOE_STAGE_SHUFFLE, 0, s));
-    STEP(launch_shuffle(c, L.nb, row_ptr, topk_slot, in->tok, w->lut, o, s));
+    STEP(launch_shuffle(c, L.nb, L.tpb, row_ptr, topk_slot, in->tok, w->lut, o, s));
     STEP(record(X, MOE_STAGE_SHUFFLE, 1, s));
     STEP(record(X, MOE_STAGE_GATHER, 0, s));
     if (x_sorted) STEP(launch_gather(c, in->x, row_ptr, o.a2s, x_sorted, s));

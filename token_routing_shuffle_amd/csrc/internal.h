@@ -10,7 +10,11 @@
 namespace moe {
 
 // Tokens per block of the histogram / scatter kernels of the shuffle.
-constexpr int kShuffleTPB = 256;
+// (Measured: 64-token blocks at T = 4096 were slower overall, the larger
+// count table costing the single-block scan more than the shorter blocks
+// gained.)
+constexpr int kShuffleMaxTPB = 256;
+inline int shuffle_tpb(int, int, int) { return kShuffleMaxTPB; }
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 inline int ilog2(int v) { int r = 0; while ((1 << r) < v) ++r; return r; }
@@ -24,7 +28,7 @@ struct WsLayout {
     size_t x_sorted, h, h_sh, y_sorted, y_sh;     // expert FFN buffers
     size_t gemm_ctr;                              // grouped-GEMM tile counters
     size_t shuffle_need, ffn_need, total;
-    int nb;                                       // shuffle blocks
+    int nb, tpb;                                  // shuffle blocks, tokens per block
 };
 
 WsLayout ws_layout(const moe_cfg& c);
@@ -43,7 +47,7 @@ struct ShuffleOut {
     int32_t *g_pred, *hist, *thist;
     int32_t* gemm_ctr;  // [16] grouped-GEMM tile counters to zero, or nullptr
 };
-hipError_t launch_shuffle(const moe_cfg& c, int nb, const int32_t* row_ptr,
+hipError_t launch_shuffle(const moe_cfg& c, int nb, int tpb, const int32_t* row_ptr,
                           const int32_t* topk_slot, const int32_t* tok, const int32_t* lut,
                           const ShuffleOut& o, hipStream_t s);
 hipError_t launch_gather(const moe_cfg& c, const void* x, const int32_t* row_ptr,

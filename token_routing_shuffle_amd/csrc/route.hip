@@ -13,7 +13,8 @@ namespace moe {
 namespace {
 
 constexpr int kBM = 16;        // tokens per block
-constexpr int kThreads = 256;  // 4 waves
+constexpr int kThreads = 512;  // 8 waves
+constexpr int kWaves = kThreads / 64;
 
 struct RouteParams {
     int T, H, E, V, n_pref, k_max, ragged, gate, renorm;
@@ -84,9 +85,9 @@ __global__ __launch_bounds__(kThreads) void k_route(RouteParams p)
     __shared__ float s_log[kBM][EP + 4];
     __shared__ int s_s2o[EP];
     __shared__ int s_o2s[EP];
-    __shared__ float s_key[4][EP];
-    __shared__ float s_gs[4][64];
-    constexpr int kSK = NTW == 1 ? 4 : (NTW == 2 ? 2 : 1);
+    __shared__ float s_key[kWaves][EP];
+    __shared__ float s_gs[kWaves][64];
+    constexpr int kSK = NTW >= kWaves ? 1 : kWaves / NTW;
     __shared__ float s_part[kSK > 1 ? kSK : 1][kBM][kSK > 1 ? EP : 1];
 
     const int tid = threadIdx.x;
@@ -133,8 +134,8 @@ __global__ __launch_bounds__(kThreads) void k_route(RouteParams p)
         // complete; only the summation order is the hardware's).
         // Waves split the chunks (SK ways, interleaved) and the column tiles
         // (SN ways); partial sums over the K split are added in wave order.
-        constexpr int SK = NTW == 1 ? 4 : (NTW == 2 ? 2 : 1);
-        constexpr int SN = 4 / SK;
+        constexpr int SK = kSK;
+        constexpr int SN = kWaves / SK;
         constexpr int TPW = NTW * 4 / SN;   // 16-column tiles per wave
         constexpr int U = TPW <= 4 ? 4 : 1; // chunks in flight per iteration
         const int wk = w % SK, wn = w / SK;
@@ -239,8 +240,8 @@ __global__ __launch_bounds__(kThreads) void k_route(RouteParams p)
     const bool sigm = p.gate == MOE_GATE_SIGMOID_GROUPED;
     const bool grouped = sigm && p.n_rgroups > 1 && p.topk_rgroups < p.n_rgroups;
     const int gsize = grouped ? E / p.n_rgroups : E;
-    for (int it = 0; it < kBM / 4; ++it) {
-        const int row = w + 4 * it;
+    for (int it = 0; it < kBM / kWaves; ++it) {
+        const int row = w + kWaves * it;
         const int t = t0 + row;
         const bool active = t < T;  // wave-uniform
         const int kt = s_kt[row];

@@ -24,12 +24,11 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTPB = kShuffleTPB;      // tokens per block
-constexpr int kTPW = kTPB / 4;         // tokens per wave (scatter)
+constexpr int kMaxTPB = kShuffleMaxTPB; // tokens per block (at most)
 constexpr int kMaxBuckets = 4096;      // E * P
 
 struct ShParams {
-    int T, E, P, V, nb, nbk, log2_epg, bucket_bits, group_bits, k_max;
+    int T, E, P, V, nb, tpb, nbk, log2_epg, bucket_bits, group_bits, k_max;
     const int32_t* row_ptr;
     const int32_t* slot;
     const int32_t* tok;
@@ -42,7 +41,7 @@ __global__ __launch_bounds__(kThreads) void k_hist(ShParams p)
     __shared__ int cnt[kMaxBuckets];
     __shared__ int tcnt[64];
     const int b = blockIdx.x;
-    const int t0 = b * kTPB, t1 = min(p.T, t0 + kTPB);
+    const int t0 = b * p.tpb, t1 = min(p.T, t0 + p.tpb);
     for (int i = threadIdx.x; i < p.nbk; i += kThreads) cnt[i] = 0;
     if (threadIdx.x < 64) tcnt[threadIdx.x] = 0;
     __syncthreads();
@@ -105,14 +104,18 @@ __global__ __launch_bounds__(1024) void k_scan(ShParams p)
     // the grouped GEMMs' tile counters start from zero for the layer
     if (p.o.gemm_ctr != nullptr && threadIdx.x < 16) p.o.gemm_ctr[threadIdx.x] = 0;
     __shared__ int smem[17];
-    __shared__ int s_total;
+    __shared__ int s_start[kMaxBuckets + 1];
     const int n = p.nbk * p.nb;
     const int A = block_scan_inplace(p.o.hist, n, smem);   // hist -> global offsets
     const int T = block_scan_inplace(p.o.thist, p.P * p.nb, smem);
-    if (threadIdx.x == 0) s_total = A;
+    // bucket b = s*P + g starts at hist[b*nb]; the end of the last bucket is
+    // A.  (This block wrote those offsets; its own writes are visible to it
+    // after the barrier.)
     __syncthreads();
-    // bucket b = s*P + g starts at hist[b*nb]; the end of the last bucket is A
-    auto bstart = [&](int bk) { return bk < p.nbk ? p.o.hist[(size_t)bk * p.nb] : s_total; };
+    for (int bk = threadIdx.x; bk <= p.nbk; bk += 1024)
+        s_start[bk] = bk < p.nbk ? p.o.hist[(size_t)bk * p.nb] : A;
+    __syncthreads();
+    auto bstart = [&](int bk) { return s_start[bk]; };
     const int E = p.E, P = p.P, epg = E / P;
     for (int s = threadIdx.x; s <= E; s += 1024) {
         const int off = bstart(s * P);
@@ -138,12 +141,13 @@ __global__ __launch_bounds__(kThreads) void k_scatter(ShParams p)
 {
     __shared__ int base[4][kMaxBuckets];
     __shared__ int tbase[4][64];
-    __shared__ int s_rp[kTPB + 1];
+    __shared__ int s_rp[kMaxTPB + 1];
     const int b = blockIdx.x;
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const int t0 = b * kTPB, t1 = min(p.T, t0 + kTPB);
+    const int t0 = b * p.tpb, t1 = min(p.T, t0 + p.tpb);
     const int nt = t1 - t0;
-    const int tw0 = min(t1, t0 + w * kTPW), tw1 = min(t1, t0 + (w + 1) * kTPW);
+    const int tpw = p.tpb / 4;   // tokens per wave
+    const int tw0 = min(t1, t0 + w * tpw), tw1 = min(t1, t0 + (w + 1) * tpw);
     const int nbk = p.nbk, P = p.P;
 
     for (int i = threadIdx.x; i < 4 * nbk; i += kThreads) base[i / nbk][i % nbk] = 0;
@@ -270,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void k_row_tok(int T, int A_max,
 
 }  // namespace
 
-hipError_t launch_shuffle(const moe_cfg& c, int nb, const int32_t* row_ptr,
+hipError_t launch_shuffle(const moe_cfg& c, int nb, int tpb, const int32_t* row_ptr,
                           const int32_t* topk_slot, const int32_t* tok, const int32_t* lut,
                           const ShuffleOut& o, hipStream_t s)
 {
@@ -280,6 +284,7 @@ hipError_t launch_shuffle(const moe_cfg& c, int nb, const int32_t* row_ptr,
     p.P = c.P;
     p.V = c.V;
     p.nb = nb;
+    p.tpb = tpb;
     p.nbk = c.E * c.P;
     p.log2_epg = ilog2(c.E / c.P);
     p.bucket_bits = ilog2(p.nbk);
