@@ -11,8 +11,9 @@
 // segments [e_begin, e_end) and (optionally) the shared experts over all T
 // rows.  Tiles are ordered (segment, n-tile, m-tile) so the m-tiles that
 // share a weight tile are adjacent, and the list is cut into 8 contiguous
-// chunks, one per XCD (workgroup i runs on XCD i % 8), so weight tiles are
-// reused from that XCD's L2.
+// chunks of equal work, one per XCD (workgroup i runs on XCD i % 8), so weight
+// tiles are reused from that XCD's L2.  An XCD's workgroups claim its tiles
+// from a counter; once it is exhausted they claim from the other XCDs'.
 //
 // Tiles are 256 x BN (BN = 256, or 128 when N does not split into 256-wide
 // tiles); the last m-tile of a segment runs with the smallest height of 64,
@@ -187,7 +188,7 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
     __shared__ int s_row0[kMaxSeg];
     __shared__ int s_cnt[kMaxSeg];
     __shared__ int s_smem[17];
-    __shared__ int s_bound[2];
+    __shared__ int s_bound[9];  // chunk start of each XCD, then the tile count
     __shared__ int s_tile;
 
     const int tid = threadIdx.x;
@@ -196,8 +197,8 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
     const int nseg = p.n_routed + p.has_shared;
     const int xcd = blockIdx.x & 7;
 
-    // ---- tile list over segments.  A tile's work is its k-steps times its
-    // height in 64-row units.
+    // ---- tile list over segments.  A tile's work is its k-steps times a
+    // weight of its height (tile_w).
     auto seg_geom = [&](int i, int& row0, int& cnt, int& nt, int& kt) {
         if (i < p.n_routed) {
             const int e = p.e_begin + i;
@@ -219,9 +220,14 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
         const int mt = (cnt + BM - 1) / BM;
         return ((cnt + mt - 1) / mt + 63) / 64 * 64;
     };
+    // Work of one k-step of an m-tile of height h, in units fitted to the
+    // measured k-step times of 192- and 256-row tiles (about 0.8 : 1): the
+    // MFMA work grows with h, the fixed part (barriers, B fragment reads,
+    // DMA of the B rows) does not.
+    auto tile_w = [&](int h) { return h / 16 + 6; };
     auto ntile_work = [&](int cnt, int kt) {
         const int mt = (cnt + BM - 1) / BM;
-        return mt * (mtile_h(cnt) / 64) * kt;
+        return mt * tile_w(mtile_h(cnt)) * kt;
     };
     {
         constexpr int SPT = (kMaxSeg + kThreads - 1) / kThreads;
@@ -260,13 +266,16 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
             s_wpref[nseg] = wtot;
         }
         __syncthreads();
-        // This XCD's share: the tiles whose work starts in
-        // [total * xcd / 8, total * (xcd + 1) / 8).  Workgroup i runs on XCD
-        // i % 8; the XCD's workgroups take its tiles in list order from a
-        // counter (tiles differ in length, so a static split would leave
-        // some workgroups idle at the end).
-        if (tid < 2) {
-            const long long target = ((long long)wtot * (xcd + tid)) >> 3;
+        // Chunk starts of the eight XCDs: XCD x owns the tiles whose work
+        // starts in [total * x / 8, total * (x + 1) / 8).  Workgroup i runs
+        // on XCD i % 8; the XCD's workgroups take its tiles from its counter
+        // (tiles differ in length, so a static split would leave some
+        // workgroups idle at the end).  A workgroup whose XCD has run out
+        // continues on the next XCDs' counters.  The up projection walks each
+        // chunk from its end, the down projection from its start (each order
+        // measured the faster one for that GEMM).
+        if (tid < 9) {
+            const long long target = ((long long)wtot * tid) >> 3;
             int b = ttot;
             if (target < wtot) {
                 int lo = 0, hi = nseg - 1;
@@ -280,20 +289,30 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
                 const int wn_ = ntile_work(cnt, kt);
                 const int rem = (int)(target - s_wpref[lo]);
                 const int n = rem / wn_;
-                const int m = min((rem % wn_) / ((mtile_h(cnt) / 64) * kt), mt - 1);
+                const int m = min((rem % wn_) / (tile_w(mtile_h(cnt)) * kt), mt - 1);
                 b = s_pref[lo] + n * mt + m;
             }
             s_bound[tid] = b;
         }
         __syncthreads();
     }
-    const int L0 = s_bound[0], L1 = s_bound[1];
+    // tile claims (thread 0): the tile for counter value v of XCD
+    // (xcd + src) & 7, else the next XCDs'; -1 when all are done
+    int src = 0;
+    auto claim = [&]() -> int {
+        for (;;) {
+            const int y = (xcd + src) & 7;
+            const int v = atomicAdd(&p.ctr[y], 1);
+            if (v < s_bound[y + 1] - s_bound[y]) return UP ? s_bound[y + 1] - 1 - v : s_bound[y] + v;
+            if (++src == 8) return -1;
+        }
+    };
 
     for (;;) {
-        if (tid == 0) s_tile = atomicAdd(&p.ctr[xcd], 1);
+        if (tid == 0) s_tile = claim();
         __syncthreads();
-        const int L = L0 + s_tile;
-        if (L >= L1) break;
+        const int L = __builtin_amdgcn_readfirstlane(s_tile);
+        if (L < 0) break;
         // ---- locate the tile
         int lo = 0, hi = nseg - 1;
         while (lo < hi) {
