@@ -162,6 +162,7 @@ def main():
     }
 
     srs_sag = time_srs_sag(cfg, c, tables, args, torch, np, moe, wl, dev)
+    share = group_share(cfg, c, d, x, tok, row_ptr, topk_slot, ws, args, torch, np, moe, dev)
     cosched = coschedule(cfg, c, tables, prof, tok, row_ptr, topk_slot, d["lut"], torch, np, moe, dev)
 
     cpu = None
@@ -195,6 +196,7 @@ def main():
         "secondary": secondary,
         "roofline": roofline,
         "srs_sag": srs_sag,
+        "group_share": share,
         "coschedule": cosched,
         "cpu_baseline": cpu,
     }
@@ -234,6 +236,58 @@ def time_srs_sag(cfg, c, tables, args, torch, np, moe, wl, dev):
                      "avg_launch_ms": round(ms, 4)}
     res["partials"] = P
     return res
+
+
+def group_share(cfg, c, d, x, tok, row_ptr, topk_slot, ws, args, torch, np, moe, dev):
+    """One device's share under expert parallelism with P = EP devices: the
+    routed expert FFN (GEMM1 + SwiGLU + GEMM2) over one placement group's
+    slot range [g*E/P, (g+1)*E/P) with that group's real rows of this layer,
+    timed with HIP events for every group (the slowest bounds an EP layer),
+    next to the same call over all E slots."""
+    T, H, E, P, I = cfg.T, cfg.H, cfg.E, cfg.P, cfg.I
+    A_max = T * cfg.k
+    i32 = dict(dtype=torch.int32, device=dev)
+    o = {n: torch.empty(k, **i32) for n, k in (
+        ("expert_count", E), ("expert_off", E + 1), ("group_count", P), ("group_off", P + 1),
+        ("pair_count", P * P), ("tok_perm", T), ("tok_off", P + 1), ("s2a", A_max), ("a2s", A_max))}
+    xs = torch.empty((A_max, H), dtype=x.dtype, device=dev)
+    moe.moe_shuffle(c, row_ptr, topk_slot, tok, d["lut"], x, o["expert_count"], o["expert_off"],
+                    o["group_count"], o["group_off"], o["pair_count"], o["tok_perm"], o["tok_off"],
+                    o["s2a"], o["a2s"], xs, ws)
+    y = torch.empty_like(xs)
+    off = o["expert_off"]
+    counts = o["expert_count"].cpu().numpy()
+    epg = E // P
+    reps = max(5, min(args.steps, 50))
+
+    def timed(e0, e1):
+        for _ in range(3):
+            moe.moe_expert_ffn(c, moe.MOE_FFN_ROUTED, xs, None, None, None, off, d["W13"], d["W2"],
+                               e0, e1, y, ws)
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(reps):
+            moe.moe_expert_ffn(c, moe.MOE_FFN_ROUTED, xs, None, None, None, off, d["W13"], d["W2"],
+                               e0, e1, y, ws)
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps
+
+    groups = []
+    for g in range(P):
+        rows = int(counts[g * epg:(g + 1) * epg].sum())
+        ms = timed(g * epg, (g + 1) * epg)
+        fl = 6.0 * rows * H * I
+        groups.append({"group": g, "rows": rows, "ms": round(ms, 4),
+                       "tflops": round(fl / (ms * 1e-3) / 1e12, 1)})
+    all_ms = timed(0, E)
+    rows_all = int(counts.sum())
+    slow = max(groups, key=lambda r: r["ms"])
+    return {"experts_per_group": epg, "reps": reps, "groups": groups,
+            "slowest_group_ms": slow["ms"], "slowest_group_rows": slow["rows"],
+            "all_slots_ms": round(all_ms, 4), "all_slots_rows": rows_all,
+            "all_slots_tflops": round(6.0 * rows_all * H * I / (all_ms * 1e-3) / 1e12, 1),
+            "note": "routed experts only; 6*rows*H*I flops per call"}
 
 
 def coschedule(cfg, c, tables, prof, tok, row_ptr, topk_slot, lut0, torch, np, moe, dev):
