@@ -38,7 +38,7 @@ hipError_t launch_row_ptr(const moe_cfg& c, const int32_t* k_tok, int32_t* row_p
                           hipStream_t s);
 hipError_t launch_route(const moe_cfg& c, const void* x, const void* Wg, const float* ebias,
                         const int32_t* slot_to_orig, const int32_t* tok, const int32_t* pref,
-                        const int32_t* k_tok, const int32_t* row_ptr, int32_t* topk_slot,
+                        const int32_t* k_tok, int32_t* row_ptr, int32_t* topk_slot,
                         float* topk_w, float* logits, hipStream_t s);
 
 struct ShuffleOut {

@@ -27,7 +27,7 @@ struct RouteParams {
     const int32_t* tok;
     const int32_t* pref;
     const int32_t* k_tok;
-    const int32_t* row_ptr;
+    int32_t* row_ptr;   // read when ragged (k_row_ptr wrote it), else written here
     int32_t* topk_slot;
     float* topk_w;
     float* logits;
@@ -100,7 +100,13 @@ __global__ __launch_bounds__(kThreads) void k_route(RouteParams p)
     for (int s = tid; s < EP; s += kThreads) s_s2o[s] = s < E ? clampi(p.s2o[s], 0, E - 1) : s;
     if (tid < kBM) {
         const int t = t0 + tid;
-        s_rp[tid] = t < T ? p.row_ptr[t] : 0;
+        if (p.ragged) {
+            s_rp[tid] = t < T ? p.row_ptr[t] : 0;
+        } else {  // fixed k: the CSR offsets are t * k, written by the token's block
+            s_rp[tid] = t * p.k_max;
+            if (t < T) p.row_ptr[t] = t * p.k_max;
+            if (t == T - 1) p.row_ptr[T] = T * p.k_max;
+        }
         s_kt[tid] = t >= T ? 0 : (p.ragged ? clampi(p.k_tok[t], 0, p.k_max) : p.k_max);
     }
     // the affinity table is read before the GEMM so its latency overlaps it
@@ -386,13 +392,15 @@ hipError_t launch_route_t(const RouteParams& p, hipStream_t s)
 
 hipError_t launch_row_ptr(const moe_cfg& c, const int32_t* k_tok, int32_t* row_ptr, hipStream_t s)
 {
+    // with a fixed k and T > 0 the route kernel writes row_ptr itself
+    if (!c.ragged && c.T > 0) return hipSuccess;
     hipLaunchKernelGGL(k_row_ptr, dim3(1), dim3(1024), 0, s, c.T, c.k_max, c.ragged, k_tok, row_ptr);
     return hipGetLastError();
 }
 
 hipError_t launch_route(const moe_cfg& c, const void* x, const void* Wg, const float* ebias,
                         const int32_t* slot_to_orig, const int32_t* tok, const int32_t* pref,
-                        const int32_t* k_tok, const int32_t* row_ptr, int32_t* topk_slot,
+                        const int32_t* k_tok, int32_t* row_ptr, int32_t* topk_slot,
                         float* topk_w, float* logits, hipStream_t s)
 {
     if (c.T == 0) return hipSuccess;

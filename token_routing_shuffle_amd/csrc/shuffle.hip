@@ -64,7 +64,9 @@ __global__ __launch_bounds__(kThreads) void k_hist(ShParams p)
 // In-place exclusive scan of n ints (one block of 1024 threads); returns
 // the total.  16 consecutive entries per thread per pass, all loaded before
 // they are summed, so a pass costs about one memory latency.
-MOE_DEV int block_scan_inplace(int32_t* a, int n, int* smem)
+// Exclusive scan of a[0, n) in place by one block; every offset that starts
+// a run of nb entries (i % nb == 0) is also stored to first[i / nb].
+MOE_DEV int block_scan_inplace(int32_t* a, int n, int nb, int* first, int* smem)
 {
     constexpr int kItems = 16;
     int carry = 0;
@@ -89,10 +91,18 @@ MOE_DEV int block_scan_inplace(int32_t* a, int n, int* smem)
         for (int q = 0; q < kItems; ++q) sum += v[q];
         int total;
         int run = carry + block_excl_scan(sum, smem, &total);
+        int r = i0 % nb, f = i0 / nb;  // position of i0 + q within its run of nb
 #pragma unroll
         for (int q = 0; q < kItems; ++q) {
-            if (i0 + q < n) a[i0 + q] = run;
+            if (i0 + q < n) {
+                a[i0 + q] = run;
+                if (r == 0) first[f] = run;
+            }
             run += v[q];
+            if (++r == nb) {
+                r = 0;
+                ++f;
+            }
         }
         carry += total;
     }
@@ -104,16 +114,16 @@ __global__ __launch_bounds__(1024) void k_scan(ShParams p)
     // the grouped GEMMs' tile counters start from zero for the layer
     if (p.o.gemm_ctr != nullptr && threadIdx.x < 16) p.o.gemm_ctr[threadIdx.x] = 0;
     __shared__ int smem[17];
-    __shared__ int s_start[kMaxBuckets + 1];
+    __shared__ int s_start[kMaxBuckets + 1];  // first offset of each bucket, then A
+    __shared__ int s_tstart[65];              // first offset of each predicted group, then T
     const int n = p.nbk * p.nb;
-    const int A = block_scan_inplace(p.o.hist, n, smem);   // hist -> global offsets
-    const int T = block_scan_inplace(p.o.thist, p.P * p.nb, smem);
-    // bucket b = s*P + g starts at hist[b*nb]; the end of the last bucket is
-    // A.  (This block wrote those offsets; its own writes are visible to it
-    // after the barrier.)
-    __syncthreads();
-    for (int bk = threadIdx.x; bk <= p.nbk; bk += 1024)
-        s_start[bk] = bk < p.nbk ? p.o.hist[(size_t)bk * p.nb] : A;
+    // hist -> global offsets; bucket b = s*P + g starts at hist[b*nb]
+    const int A = block_scan_inplace(p.o.hist, n, p.nb, s_start, smem);
+    const int T = block_scan_inplace(p.o.thist, p.P * p.nb, p.nb, s_tstart, smem);
+    if (threadIdx.x == 0) {
+        s_start[p.nbk] = A;
+        s_tstart[p.P] = T;
+    }
     __syncthreads();
     auto bstart = [&](int bk) { return s_start[bk]; };
     const int E = p.E, P = p.P, epg = E / P;
@@ -126,7 +136,7 @@ __global__ __launch_bounds__(1024) void k_scan(ShParams p)
         const int off = bstart(g * epg * P);
         p.o.group_off[g] = off;
         if (g < P) p.o.group_count[g] = bstart((g + 1) * epg * P) - off;
-        p.o.tok_off[g] = g < P ? p.o.thist[g * p.nb] : T;
+        p.o.tok_off[g] = s_tstart[g];
     }
     // pair_count[pg * P + g]: predicted group pg, expert group g
     for (int i = threadIdx.x; i < P * P; i += 1024) {
