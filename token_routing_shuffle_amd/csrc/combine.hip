@@ -3,9 +3,12 @@
 // German summary, technical summary §2B; Japanese summary, technical overview
 // §2.2B), plus the shared-expert output.
 //
-// Gather-style and deterministic: one wave per token reads its k_t rows of
-// y_sorted through assign_to_sorted, accumulates w * y in fp32 in j order,
-// adds y_sh and writes the row once.  No atomics.
+// Gather-style and deterministic: each wave takes 64 16-byte chunks (1 KB)
+// of one token's row, reads them from the token's k_t rows of y_sorted
+// through assign_to_sorted, accumulates w * y in fp32 in j order, adds y_sh
+// and writes them once.  No atomics.  A token's row is split over
+// ceil(H / 512) waves (bf16) so that many small, independent waves keep the
+// HBM busy.
 #include "common.h"
 #include "internal.h"
 
@@ -22,13 +25,17 @@ __global__ __launch_bounds__(kThreads) void k_combine(int T, int H, const void* 
                                                       const void* __restrict__ ysh,
                                                       void* __restrict__ out)
 {
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-    const int l = threadIdx.x & 63;
-    if (t >= T) return;
     constexpr int EPC = BF16 ? 8 : 4;  // elements per 16-byte chunk
     const int nch = H / EPC;
+    const int nq = (nch + 63) / 64;    // waves per token
+    const int wid = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int t = wid / nq;
+    const int l = threadIdx.x & 63;
+    if (t >= T) return;
     const int a0 = row_ptr[t], a1 = row_ptr[t + 1];
-    for (int c = l; c < nch; c += 64) {
+    {
+        const int c = (wid % nq) * 64 + l;
+        if (c >= nch) return;
         float acc[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
@@ -92,7 +99,8 @@ hipError_t launch_combine(const moe_cfg& c, const void* y_sorted, const int32_t*
                           void* out, hipStream_t s)
 {
     if (c.T == 0) return hipSuccess;
-    const dim3 grid(ceil_div(c.T, 4)), block(kThreads);
+    const int nq = ceil_div(c.H / (c.dtype == MOE_BF16 ? 8 : 4), 64);
+    const dim3 grid((unsigned)ceil_div(c.T * nq, 4)), block(kThreads);
     if (c.dtype == MOE_BF16)
         hipLaunchKernelGGL(k_combine<true>, grid, block, 0, s, c.T, c.H, y_sorted, a2s, row_ptr,
                            topk_w, y_sh, out);
