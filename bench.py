@@ -61,8 +61,8 @@ def algorithmic(cfg, A):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the sharding design is described in DESIGN.md); run with --gpus 1",
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(collectives are not implemented); run with --gpus 1",
               file=sys.stderr)
         sys.exit(2)
 

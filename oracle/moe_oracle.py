@@ -34,7 +34,8 @@ Services via Model-System Co-Designs", Korean summary):
 
 Everything the pages leave open (gate function, top-k rule and tie-break,
 SwiGLU expert form, shared experts, weight normalisation) follows the layer
-configurations' own description; the readings are listed in the design doc.
+configurations' own description (the named models' published layer forms);
+each function's docstring states the choice it makes.
 """
 from __future__ import annotations
 
