@@ -34,6 +34,9 @@ def parse():
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--fuse-gather", type=int, default=int(os.environ.get("MOE_BENCH_FUSE_GATHER", "1")))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the sections after the layer (SRS/SAG, one device's share, "
+                         "co-scheduling), e.g. for a per-kernel profile of the layer alone")
     ap.add_argument("--cpu-sample", type=int, default=4096,
                     help="tokens in the oracle's timed sample (capped at the layer's T)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
@@ -161,9 +164,12 @@ def main():
         if args.fuse_gather == 0 else None,
     }
 
-    srs_sag = time_srs_sag(cfg, c, tables, args, torch, np, moe, wl, dev)
-    share = group_share(cfg, c, d, x, tok, row_ptr, topk_slot, ws, args, torch, np, moe, dev)
-    cosched = coschedule(cfg, c, tables, prof, tok, row_ptr, topk_slot, d["lut"], torch, np, moe, dev)
+    srs_sag = share = cosched = None
+    if not args.no_extras:
+        srs_sag = time_srs_sag(cfg, c, tables, args, torch, np, moe, wl, dev)
+        share = group_share(cfg, c, d, x, tok, row_ptr, topk_slot, ws, args, torch, np, moe, dev)
+        cosched = coschedule(cfg, c, tables, prof, tok, row_ptr, topk_slot, d["lut"], torch, np, moe,
+                             dev)
 
     cpu = None
     if not args.no_cpu_baseline:
