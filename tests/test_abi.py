@@ -64,6 +64,21 @@ def test_every_workload_config_validates(m):
         assert m.moe_workspace_bytes(c) > 0
 
 
+def test_profiling_chunks_validate(m):
+    """The offline profile routes its 65536-token draw in chunks; every
+    chunk's layer configuration must pass validation (k = 32 layers allow
+    at most 16383 tokens per call), and one more token must not."""
+    from token_routing_shuffle_amd import offline
+    from token_routing_shuffle_amd import workload as wl
+    for name, cfg in wl.CONFIGS.items():
+        n = offline.route_chunk(cfg)
+        assert 1 <= n <= 16384
+        assert m.moe_validate(m.make_cfg(cfg, T=n)) == m.MOE_OK, (name, n, m.moe_last_error())
+        if n < 16384:
+            assert m.moe_validate(m.make_cfg(cfg, T=n + 1)) == m.MOE_ESHAPE, name
+    assert offline.route_chunk(wl.CONFIGS["prism"]) == 16383
+
+
 @pytest.mark.parametrize("field,value,code", [
     ("E", 12, "MOE_ESHAPE"),            # E/P = 1.5
     ("P", 3, "MOE_ESHAPE"),             # E % P != 0

@@ -44,13 +44,27 @@ def device_layer(cfg, tables, w: dict, lut: np.ndarray, device="cuda") -> dict:
     return d
 
 
+def route_chunk(cfg, chunk: int = 16384) -> int:
+    """Largest token count <= chunk whose layer configuration passes
+    moe_validate's bf16 operand limit (every GEMM row operand below 2 GiB:
+    T*k*max(H, I)*2 and T*max(H, ns*Is)*2)."""
+    if cfg.dtype != "bf16":
+        return chunk
+    k_routed = max(cfg.H, cfg.I)
+    k_shared = max(cfg.H, cfg.n_shared * cfg.I_shared)
+    cap = min((2 ** 31 - 1) // (2 * cfg.k * k_routed), (2 ** 31 - 1) // (2 * k_shared))
+    return max(1, min(chunk, cap))
+
+
 def profile_routing(cfg, dev: dict, prof_x: torch.Tensor, prof_tok: np.ndarray,
                     chunk: int = 16384):
-    """Route a profiling draw with moe_route (chunks of `chunk` tokens) and
-    return the whole draw's routing as device CSR (row_ptr [n+1], slots [A])
-    plus its token IDs (device int32)."""
+    """Route a profiling draw with moe_route (chunks of at most `chunk`
+    tokens, fewer where the layer's operand limit requires) and return the
+    whole draw's routing as device CSR (row_ptr [n+1], slots [A]) plus its
+    token IDs (device int32)."""
     device = prof_x.device
     n = prof_x.shape[0]
+    chunk = route_chunk(cfg, chunk)
     tok_all = torch.as_tensor(np.asarray(prof_tok, np.int32), device=device)
     rps, sls, base = [torch.zeros(1, dtype=torch.int32, device=device)], [], 0
     for s in range(0, n, chunk):
