@@ -129,6 +129,10 @@ int32_t moe_validate(const moe_cfg* cfg);
  * cfg is invalid). */
 size_t moe_workspace_bytes(const moe_cfg* cfg);
 
+/* Workspace bytes moe_route needs for this layer (0: none; also 0 when cfg
+ * is invalid, see moe_validate).  Host only.  moe_workspace_bytes covers it. */
+size_t moe_route_workspace_bytes(const moe_cfg* cfg);
+
 /* Text of the last error on the calling thread (never NULL). */
 const char* moe_last_error(void);
 
@@ -155,7 +159,11 @@ const char* moe_last_error(void);
  *   topk_w[A_max]   fp32 weights: softmax p_j (renorm: p_j / sum of selected
  *                   p); sigmoid: route_scale * s_j / sum_j s_j, s = sigmoid(l)
  *   logits[T,E]     optional fp32 export of the biased logits, slot order
- * Workspace: unused (may be NULL).
+ * Workspace: moe_route_workspace_bytes(cfg) bytes (device, 256-byte
+ * aligned), or NULL when that is 0.  bf16 layers with E >= 128 run the gate
+ * GEMM as its own tiled kernel and keep its fp32 partial logits there; every
+ * other layer computes the gate inside the route kernel.  MOE_EWORKSPACE if
+ * it is missing or too small.
  */
 int32_t moe_route(const moe_cfg* cfg, const void* x, const void* Wg, const float* ebias,
                   const int32_t* slot_to_orig, const int32_t* tok, const int32_t* pref,

@@ -30,6 +30,7 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "moe_combine", "moe_expert_ffn", "moe_forward", "moe_last_error", "moe_route",
         "moe_sag", "moe_shuffle", "moe_srs", "moe_validate", "moe_workspace_bytes",
+        "moe_route_workspace_bytes",
         "moe_token_group_counts", "moe_lut_from_counts", "moe_expert_group_counts",
         "moe_balanced_assign", "moe_optimize_placement", "moe_request_group_hist"])
 
@@ -167,6 +168,28 @@ def test_calls_reject_misaligned_tensors(m):
     rc = L.moe_route(ctypes.byref(c), fake + 2, fake, None, fake, fake, None, None, fake, fake,
                      fake, None, None, 0, None)
     assert rc == m.MOE_EINVAL and "aligned" in m.moe_last_error()
+
+
+def test_route_workspace(m):
+    """bf16 layers with E >= 128 need a route workspace (the tiled gate GEMM's
+    partial logits, within the layer workspace); moe_route rejects a missing
+    one before launching anything; E = 64 and fp32 layers need none."""
+    cf = _cfgs(m)
+    for name in ("tiny", "dsv2lite"):
+        assert m.moe_route_workspace_bytes(cf[name]) == 0, name
+    for name in ("qwen3", "prism", "dsv3_decode", "dsv3_prefill"):
+        c = cf[name]
+        n = m.moe_route_workspace_bytes(c)
+        assert n >= c.T * c.E * 4, name
+        assert n <= m.moe_workspace_bytes(c), name
+    c = cf["qwen3"]
+    fake = 1 << 40
+    rc = m.lib().moe_route(ctypes.byref(c), fake, fake, None, fake, fake, None, None, fake, fake,
+                           fake, None, None, 0, None)
+    assert rc == m.MOE_EWORKSPACE
+    bad = _cfgs(m)["qwen3"]
+    bad.E = 12
+    assert m.moe_route_workspace_bytes(bad) == 0
 
 
 def test_workspace_grows_with_tokens_and_shrinks_with_fused_gather(m):

@@ -55,7 +55,7 @@ def gpu_route(c, fuse=0):
     row_ptr, slot, wt = hn.dev_i32(T + 1), hn.dev_i32(A), hn.dev_f32(A)
     logits = hn.dev_f32(T * c.cfg.E)
     m.moe_route(cfg, c.x, d["Wg"], d["ebias"], d["slot_to_orig"], tok, d["pref"], k_tok, row_ptr,
-                slot, wt, logits)
+                slot, wt, logits, ws=m.route_workspace(cfg))
     torch.cuda.synchronize()
     rp = row_ptr.cpu().numpy()
     return dict(row_ptr=rp, slot=slot.cpu().numpy()[:rp[-1]], w=wt.cpu().numpy()[:rp[-1]],

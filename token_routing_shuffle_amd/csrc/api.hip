@@ -132,6 +132,14 @@ WsLayout ws_layout(const moe_cfg& c)
     L.y_sorted = take(A * c.H * es);
     L.y_sh = take(c.n_shared > 0 ? T * c.H * es : 0);
     L.total = off;
+    // The tiled gate GEMM's partial logits live at the start of the expert
+    // FFN buffers: the route is done before the FFN writes them.
+    L.glog = L.h;
+    L.route_need = 0;
+    if (gate_tiled(c) && c.T > 0) {
+        L.route_need = L.glog + (((size_t)gate_split(c) * T * E * 4 + 255) & ~(size_t)255);
+        L.total = std::max(L.total, L.route_need);
+    }
     return L;
 }
 
@@ -176,16 +184,27 @@ MOE_API size_t moe_workspace_bytes(const moe_cfg* cfg)
 
 MOE_API const char* moe_last_error(void) { return g_err; }
 
+MOE_API size_t moe_route_workspace_bytes(const moe_cfg* cfg)
+{
+    if (check_cfg(cfg) != MOE_OK) return 0;
+    return ws_layout(*cfg).route_need;
+}
+
 MOE_API int32_t moe_route(const moe_cfg* cfg, const void* x, const void* Wg, const float* ebias,
                           const int32_t* slot_to_orig, const int32_t* tok, const int32_t* pref,
                           const int32_t* k_tok, int32_t* row_ptr, int32_t* topk_slot,
                           float* topk_w, float* logits, void* ws, size_t ws_bytes, void* stream)
 {
-    (void)ws;
-    (void)ws_bytes;
     int32_t rc = check_cfg(cfg);
     if (rc != MOE_OK) return rc;
     const moe_cfg& c = *cfg;
+    const WsLayout L = ws_layout(c);
+    float* glog = nullptr;
+    if (L.route_need > 0) {
+        rc = check_ws(ws, ws_bytes, L.route_need);
+        if (rc != MOE_OK) return rc;
+        glog = at<float>(ws, L.glog);
+    }
     REQUIRE(row_ptr);
     if (c.T > 0) {
         REQUIRE(x);
@@ -202,7 +221,7 @@ MOE_API int32_t moe_route(const moe_cfg* cfg, const void* x, const void* Wg, con
     hipError_t e = launch_row_ptr(c, k_tok, row_ptr, s);
     if (e == hipSuccess)
         e = launch_route(c, x, Wg, ebias, slot_to_orig, tok, pref, k_tok, row_ptr, topk_slot, topk_w,
-                         logits, s);
+                         logits, glog, s);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_route");
 }
 
@@ -614,7 +633,8 @@ MOE_API int32_t moe_forward(const moe_cfg* cfg, const moe_weights* w, const moe_
     STEP(record(X, MOE_STAGE_ROUTE, 0, s));
     STEP(launch_row_ptr(c, in->k_tok, row_ptr, s));
     STEP(launch_route(c, in->x, w->Wg, w->ebias, w->slot_to_orig, in->tok, w->pref, in->k_tok,
-                      row_ptr, topk_slot, topk_w, X->logits, s));
+                      row_ptr, topk_slot, topk_w, X->logits,
+                      L.route_need > 0 ? at<float>(ws, L.glog) : nullptr, s));
     STEP(record(X, MOE_STAGE_ROUTE, 1, s));
     STEP(record(X, MOE_STAGE_SHUFFLE, 0, s));
     STEP(launch_shuffle(c, L.nb, L.tpb, row_ptr, topk_slot, in->tok, w->lut, o, s));

@@ -27,11 +27,17 @@ struct WsLayout {
     size_t tok_perm, tok_off, s2a, a2s, row_tok;  // shuffle outputs / scratch
     size_t x_sorted, h, h_sh, y_sorted, y_sh;     // expert FFN buffers
     size_t gemm_ctr;                              // grouped-GEMM tile counters
+    size_t glog, route_need;                      // gate partial logits (aliases h..), route's need
     size_t shuffle_need, ffn_need, total;
     int nb, tpb;                                  // shuffle blocks, tokens per block
 };
 
 WsLayout ws_layout(const moe_cfg& c);
+
+// Route of large-E bf16 layers: the gate GEMM runs as its own tiled kernel
+// into gate_split(c) slices of partial logits (fp32 [S][T][E], workspace).
+bool gate_tiled(const moe_cfg& c);
+int gate_split(const moe_cfg& c);
 
 // --- launchers (no argument checks; callers validate) ---------------------
 hipError_t launch_row_ptr(const moe_cfg& c, const int32_t* k_tok, int32_t* row_ptr,
@@ -39,7 +45,7 @@ hipError_t launch_row_ptr(const moe_cfg& c, const int32_t* k_tok, int32_t* row_p
 hipError_t launch_route(const moe_cfg& c, const void* x, const void* Wg, const float* ebias,
                         const int32_t* slot_to_orig, const int32_t* tok, const int32_t* pref,
                         const int32_t* k_tok, int32_t* row_ptr, int32_t* topk_slot,
-                        float* topk_w, float* logits, hipStream_t s);
+                        float* topk_w, float* logits, float* glog, hipStream_t s);
 
 struct ShuffleOut {
     int32_t *expert_count, *expert_off, *group_count, *group_off, *pair_count;

@@ -31,6 +31,8 @@ struct RouteParams {
     int32_t* topk_slot;
     float* topk_w;
     float* logits;
+    const float* glog;  // [gS][T][E] partial logits of the tiled gate GEMM, or nullptr
+    int gS;
 };
 
 // CSR offsets: row_ptr[t] = sum of k over tokens < t (k_tok clamped to
@@ -65,6 +67,159 @@ __global__ __launch_bounds__(1024) void k_row_ptr(int T, int k_max, int ragged,
         carry += total;
     }
     if (threadIdx.x == 0) row_ptr[T] = carry;
+}
+
+// ---------------------------------------------------------------------------
+// Gate GEMM for large E (bf16): partial logits glog[s][t][e] = sum over the
+// K slice s of x[t,k] * Wg[e,k], a 64-token x 128-expert tile per block.
+// The fused route kernel reads all of Wg once per 16 tokens, which for E of
+// 128 and more makes its L2 traffic T/16 * E*H*2 bytes; this tiling reads Wg
+// once per 64 tokens and x once per 128 experts.  Both operands go to LDS by
+// DMA (64-wide k-chunks, 128-byte rows XOR-swizzled c ^ (row & 7), three
+// buffers: the chunk being read and the next two in flight, 72 KB, two
+// blocks per CU); four waves
+// take 16 tokens each against all 128 experts (8 MFMA 16x16x32 column tiles).
+constexpr int kGT = 64, kGE = 128, kGNB = 3;
+constexpr int kGRows = kGT + kGE;           // LDS rows per chunk
+constexpr int kGChunkE = kGRows * 64;       // bf16 elements per chunk buffer
+constexpr int kGNI = kGRows / 8 / 4;        // DMA instructions per wave per chunk
+
+#define MOE_LDS_PTR(p) ((void __attribute__((address_space(3)))*)(p))
+
+template <int N>
+MOE_DEV void g_wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int OFF>
+MOE_DEV bf16x8_t g_lds_read(uint32_t addr)
+{
+    static_assert(OFF >= 0 && OFF < 65536, "ds_read offset range");
+    bf16x8_t v;
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+#else
+    (void)addr;
+    v = bf16x8_t{};
+#endif
+    return v;
+}
+
+MOE_DEV void g_frag_wait(bf16x8_t (&a)[2], bf16x8_t (&b)[8][2])
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    asm volatile("" : "+v"(a[0]), "+v"(a[1]));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(b[i][0]), "+v"(b[i][1]));
+#else
+    (void)a;
+    (void)b;
+#endif
+}
+
+__global__ __launch_bounds__(256) void k_gate_logits(int T, int H, int E, int Kc, const uint16_t* x,
+                                                      const uint16_t* Wg, float* __restrict__ glog)
+{
+    __shared__ __attribute__((aligned(16))) uint16_t s_g[kGNB * kGChunkE];
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
+    const int t0 = blockIdx.x * kGT, e0 = blockIdx.y * kGE, ks = blockIdx.z;
+    const int nch = Kc / 64;
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, T * H * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)Wg, (short)0, E * H * 2, 0x00020000);
+    // DMA instruction q = w * kGNI + j covers LDS rows 8q..8q+7 (x rows first,
+    // then Wg rows); lane l fills row 8q + (l >> 3) at slot l & 7, which
+    // holds the row's global chunk (l & 7) ^ (row & 7).  Rows past T or E
+    // repeat the last one.
+    int doff[kGNI];
+#pragma unroll
+    for (int j = 0; j < kGNI; ++j) {
+        const int q = w * kGNI + j;
+        const int row = q * 8 + (l >> 3);
+        const int chunk = (l & 7) ^ (row & 7);
+        const int src = row < kGT ? min(t0 + row, T - 1) : min(e0 + row - kGT, E - 1);
+        doff[j] = src * H * 2 + chunk * 16;
+    }
+    auto dma = [&](int c) {
+        const int ko = (ks * Kc + c * 64) * 2;
+        uint16_t* buf = s_g + (c % kGNB) * kGChunkE;
+#pragma unroll
+        for (int j = 0; j < kGNI; ++j) {
+            const int q = w * kGNI + j;
+            uint16_t* dst = buf + q * 8 * 64;
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass cannot form LDS pointers
+            if (q * 8 < kGT)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, MOE_LDS_PTR(dst), 16, doff[j], ko, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, MOE_LDS_PTR(dst), 16, doff[j], ko, 0, 0);
+#else
+            (void)dst;
+            (void)ko;
+#endif
+        }
+    };
+    // Fragments: lane (r = l & 15, kg = l >> 4) reads row r of its 16-row
+    // block at chunks kg (first 32-wide half) and kg + 4 (second half).
+    const int r = l & 15, kg = l >> 4;
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint32_t sbase = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)s_g);
+#else
+    const uint32_t sbase = 0;
+#endif
+    const uint32_t a_row = sbase + (w * 16 + r) * 128, b_row = sbase + (kGT + r) * 128;
+    const uint32_t c0 = (uint32_t)((kg ^ (r & 7)) << 4), c1 = (uint32_t)(((kg + 4) ^ (r & 7)) << 4);
+    f32x4_t acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    dma(0);
+    if (nch > 1) dma(1);
+    for (int c = 0; c < nch; ++c) {
+        // this wave's DMA of chunk c has landed (chunk c+1's may be in flight)
+        if (c + 1 < nch) g_wait_vmcnt<kGNI>(); else g_wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();  // chunk c visible; chunk c-1's buffer free
+        if (c + 2 < nch) dma(c + 2);
+        const uint32_t so = (uint32_t)((c % kGNB) * kGChunkE * 2);
+        bf16x8_t a[2], b[8][2];
+        a[0] = g_lds_read<0>(a_row + so + c0);
+        a[1] = g_lds_read<0>(a_row + so + c1);
+        b[0][0] = g_lds_read<0 * 16 * 128>(b_row + so + c0);
+        b[0][1] = g_lds_read<0 * 16 * 128>(b_row + so + c1);
+        b[1][0] = g_lds_read<1 * 16 * 128>(b_row + so + c0);
+        b[1][1] = g_lds_read<1 * 16 * 128>(b_row + so + c1);
+        b[2][0] = g_lds_read<2 * 16 * 128>(b_row + so + c0);
+        b[2][1] = g_lds_read<2 * 16 * 128>(b_row + so + c1);
+        b[3][0] = g_lds_read<3 * 16 * 128>(b_row + so + c0);
+        b[3][1] = g_lds_read<3 * 16 * 128>(b_row + so + c1);
+        b[4][0] = g_lds_read<4 * 16 * 128>(b_row + so + c0);
+        b[4][1] = g_lds_read<4 * 16 * 128>(b_row + so + c1);
+        b[5][0] = g_lds_read<5 * 16 * 128>(b_row + so + c0);
+        b[5][1] = g_lds_read<5 * 16 * 128>(b_row + so + c1);
+        b[6][0] = g_lds_read<6 * 16 * 128>(b_row + so + c0);
+        b[6][1] = g_lds_read<6 * 16 * 128>(b_row + so + c1);
+        b[7][0] = g_lds_read<7 * 16 * 128>(b_row + so + c0);
+        b[7][1] = g_lds_read<7 * 16 * 128>(b_row + so + c1);
+        g_frag_wait(a, b);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b[i][0], acc[i], 0, 0, 0);
+            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], b[i][1], acc[i], 0, 0, 0);
+        }
+    }
+    // D layout: lane l holds expert column (l & 15) of tile i, tokens 4*kg + v
+    float* out = glog + (size_t)ks * T * E;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int e = e0 + i * 16 + r;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int t = t0 + w * 16 + kg * 4 + v;
+            if (t < T && e < E) out[(size_t)t * E + e] = acc[i][v];
+        }
+    }
 }
 
 // Winner of (ordered key desc, original id asc); sentinel uk = 0 loses to any key.
@@ -132,7 +287,19 @@ __global__ __launch_bounds__(kThreads) void k_route(RouteParams p)
     for (int s = tid; s < E; s += kThreads) s_o2s[s_s2o[s]] = s;
 
     // ---------------- gate GEMM: logits[16 tokens][E] ----------------
-    if constexpr (BF16) {
+    if (p.glog != nullptr) {
+        // from the tiled gate GEMM: partial sums added in slice order
+        for (int idx = tid; idx < kBM * EP; idx += kThreads) {
+            const int row = idx / EP, col = idx % EP;
+            const int t = t0 + row;
+            float sum = 0.0f;
+            if (t < T && col < E) {
+                sum = p.glog[(size_t)t * E + col];
+                for (int q = 1; q < p.gS; ++q) sum += p.glog[((size_t)q * T + t) * E + col];
+            }
+            s_log[row][col] = sum;
+        }
+    } else if constexpr (BF16) {
         // MFMA 16x16x32 bf16.  Lane l feeds token row (l & 15) and expert
         // column (l & 15) of its tile; its 4-lane group kg = l >> 4 owns the
         // contiguous k-range [16kg, 16kg+16) of every 64-wide chunk, split over
@@ -398,10 +565,23 @@ hipError_t launch_row_ptr(const moe_cfg& c, const int32_t* k_tok, int32_t* row_p
     return hipGetLastError();
 }
 
+bool gate_tiled(const moe_cfg& c) { return c.dtype == MOE_BF16 && c.E >= kGE; }
+
+int gate_split(const moe_cfg& c)
+{
+    // K slices: enough blocks for the chip (256 CUs), each slice at least
+    // four 64-wide chunks; the partial sums are added in slice order.
+    const long long tiles = (long long)ceil_div(c.T, kGT) * ceil_div(c.E, kGE);
+    const int nch = c.H / 64;
+    int S = 1;
+    while (tiles * S < 256 && nch % (2 * S) == 0 && nch / (2 * S) >= 4) S *= 2;
+    return S;
+}
+
 hipError_t launch_route(const moe_cfg& c, const void* x, const void* Wg, const float* ebias,
                         const int32_t* slot_to_orig, const int32_t* tok, const int32_t* pref,
                         const int32_t* k_tok, int32_t* row_ptr, int32_t* topk_slot,
-                        float* topk_w, float* logits, hipStream_t s)
+                        float* topk_w, float* logits, float* glog, hipStream_t s)
 {
     if (c.T == 0) return hipSuccess;
     RouteParams p;
@@ -430,6 +610,17 @@ hipError_t launch_route(const moe_cfg& c, const void* x, const void* Wg, const f
     p.topk_slot = topk_slot;
     p.topk_w = topk_w;
     p.logits = logits;
+    p.glog = nullptr;
+    p.gS = 1;
+    if (gate_tiled(c)) {
+        const int S = gate_split(c);
+        hipLaunchKernelGGL(k_gate_logits, dim3(ceil_div(c.T, kGT), ceil_div(c.E, kGE), S), dim3(256), 0, s,
+                           c.T, c.H, c.E, c.H / S, (const uint16_t*)x, (const uint16_t*)Wg, glog);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        p.glog = glog;
+        p.gS = S;
+    }
     return c.dtype == MOE_BF16 ? launch_route_t<true>(p, s) : launch_route_t<false>(p, s);
 }
 

@@ -76,6 +76,8 @@ def _load():
     lib.moe_validate.argtypes = [P(moe_cfg)]
     lib.moe_workspace_bytes.restype = sz
     lib.moe_workspace_bytes.argtypes = [P(moe_cfg)]
+    lib.moe_route_workspace_bytes.restype = sz
+    lib.moe_route_workspace_bytes.argtypes = [P(moe_cfg)]
     lib.moe_last_error.restype = ctypes.c_char_p
     lib.moe_last_error.argtypes = []
     lib.moe_route.restype = i32
@@ -119,7 +121,8 @@ def lib():
     return _lib
 
 
-EXPORTED = ("moe_validate", "moe_workspace_bytes", "moe_last_error", "moe_route", "moe_shuffle",
+EXPORTED = ("moe_validate", "moe_workspace_bytes", "moe_route_workspace_bytes", "moe_last_error",
+            "moe_route", "moe_shuffle",
             "moe_expert_ffn", "moe_combine", "moe_forward", "moe_srs", "moe_sag",
             "moe_token_group_counts", "moe_lut_from_counts", "moe_expert_group_counts",
             "moe_balanced_assign", "moe_optimize_placement", "moe_request_group_hist")
@@ -174,6 +177,16 @@ def moe_workspace_bytes(cfg: moe_cfg) -> int:
 
 def moe_last_error() -> str:
     return lib().moe_last_error().decode()
+
+
+def moe_route_workspace_bytes(cfg: moe_cfg) -> int:
+    return lib().moe_route_workspace_bytes(ctypes.byref(cfg))
+
+
+def route_workspace(cfg: moe_cfg, device="cuda"):
+    """Device workspace for moe_route alone (None when the layer needs none)."""
+    n = moe_route_workspace_bytes(cfg)
+    return None if n == 0 else torch.empty(n, dtype=torch.uint8, device=device)
 
 
 def workspace(cfg: moe_cfg, device="cuda"):

@@ -77,7 +77,8 @@ def profile_routing(cfg, dev: dict, prof_x: torch.Tensor, prof_tok: np.ndarray,
         slots = torch.empty(m * cfg.k, dtype=torch.int32, device=device)
         wts = torch.empty(m * cfg.k, dtype=torch.float32, device=device)
         moe.moe_route(c, prof_x[s:s + m], dev["Wg"], dev.get("ebias"), dev["slot_to_orig"],
-                      tok_all[s:s + m], dev.get("pref"), k_tok, row_ptr, slots, wts)
+                      tok_all[s:s + m], dev.get("pref"), k_tok, row_ptr, slots, wts,
+                      ws=moe.route_workspace(c, device))
         a = int(row_ptr[m].item())
         rps.append(row_ptr[1:] + base)
         sls.append(slots[:a])
