@@ -113,6 +113,9 @@ WsLayout ws_layout(const moe_cfg& c)
     L.g_pred = take(T * 4);
     L.hist = take(E * P * L.nb * 4);
     L.thist = take(P * L.nb * 4);
+    L.rowtot = take((E * P + P) * 4);
+    L.bstart = take((E * P + 1) * 4);
+    L.tstart = take((P + 1) * 4);
     L.expert_count = take(E * 4);
     L.expert_off = take((E + 1) * 4);
     L.group_count = take(P * 4);
@@ -272,6 +275,9 @@ MOE_API int32_t moe_shuffle(const moe_cfg* cfg, const int32_t* row_ptr, const in
     o.g_pred = at<int32_t>(ws, L.g_pred);
     o.hist = at<int32_t>(ws, L.hist);
     o.thist = at<int32_t>(ws, L.thist);
+    o.rowtot = at<int32_t>(ws, L.rowtot);
+    o.bstart = at<int32_t>(ws, L.bstart);
+    o.tstart = at<int32_t>(ws, L.tstart);
     o.gemm_ctr = nullptr;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_shuffle(c, L.nb, L.tpb, row_ptr, topk_slot, tok, lut, o, s);
@@ -616,6 +622,9 @@ MOE_API int32_t moe_forward(const moe_cfg* cfg, const moe_weights* w, const moe_
     o.g_pred = at<int32_t>(ws, L.g_pred);
     o.hist = at<int32_t>(ws, L.hist);
     o.thist = at<int32_t>(ws, L.thist);
+    o.rowtot = at<int32_t>(ws, L.rowtot);
+    o.bstart = at<int32_t>(ws, L.bstart);
+    o.tstart = at<int32_t>(ws, L.tstart);
     o.gemm_ctr = at<int32_t>(ws, L.gemm_ctr);   // zeroed by the shuffle for the FFN below
     void* x_sorted = c.fuse_gather ? nullptr : (X->x_sorted ? X->x_sorted : at<void>(ws, L.x_sorted));
     void* y_sorted = X->y_sorted ? X->y_sorted : at<void>(ws, L.y_sorted);

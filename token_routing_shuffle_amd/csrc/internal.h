@@ -22,7 +22,7 @@ inline int ilog2(int v) { int r = 0; while ((1 << r) < v) ++r; return r; }
 // Workspace layout (byte offsets, 256-byte aligned sections).
 struct WsLayout {
     size_t row_ptr, topk_slot, topk_w;            // route outputs (moe_forward)
-    size_t g_pred, hist, thist;                   // shuffle scratch
+    size_t g_pred, hist, thist, rowtot, bstart, tstart;  // shuffle scratch
     size_t expert_count, expert_off, group_count, group_off, pair_count;
     size_t tok_perm, tok_off, s2a, a2s, row_tok;  // shuffle outputs / scratch
     size_t x_sorted, h, h_sh, y_sorted, y_sh;     // expert FFN buffers
@@ -51,6 +51,7 @@ struct ShuffleOut {
     int32_t *expert_count, *expert_off, *group_count, *group_off, *pair_count;
     int32_t *tok_perm, *tok_off, *s2a, *a2s, *row_tok;
     int32_t *g_pred, *hist, *thist;
+    int32_t *rowtot, *bstart, *tstart;  // row totals, bucket and group starts (scratch)
     int32_t* gemm_ctr;  // [16] grouped-GEMM tile counters to zero, or nullptr
 };
 hipError_t launch_shuffle(const moe_cfg& c, int nb, int tpb, const int32_t* row_ptr,

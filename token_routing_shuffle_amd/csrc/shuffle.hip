@@ -13,10 +13,13 @@
 // counts and offsets, the P x P would-be all-to-all matrix and the token
 // permutation.
 //
-// Three kernels: per-block LDS histograms, one single-block scan over the
-// (bucket, block) table in bucket-major order, and a scatter that ranks
+// Four kernels: per-block LDS histograms; a wave per bucket that turns its
+// row of per-block counts into offsets within the bucket (and the bucket's
+// total); one block that scans the bucket totals (E*P of them) into bucket
+// starts and writes the per-slot / per-group results; a scatter that ranks
 // equal buckets inside a wave with ballots (stable: blocks, waves, chunks and
-// lanes all follow assignment order).
+// lanes all follow assignment order).  The global offset of (bucket k,
+// block b) is bucket_start[k] + (counts of k in blocks before b).
 #include "common.h"
 #include "internal.h"
 
@@ -61,52 +64,24 @@ __global__ __launch_bounds__(kThreads) void k_hist(ShParams p)
     if (threadIdx.x < p.P) p.o.thist[threadIdx.x * p.nb + b] = tcnt[threadIdx.x];
 }
 
-// In-place exclusive scan of n ints (one block of 1024 threads); returns
-// the total.  16 consecutive entries per thread per pass, all loaded before
-// they are summed, so a pass costs about one memory latency.
-// Exclusive scan of a[0, n) in place by one block; every offset that starts
-// a run of nb entries (i % nb == 0) is also stored to first[i / nb].
-MOE_DEV int block_scan_inplace(int32_t* a, int n, int nb, int* first, int* smem)
+// Rows of the count tables (buckets, then predicted groups): one wave per
+// row turns the row's per-block counts into exclusive offsets in place and
+// stores the row total.
+__global__ __launch_bounds__(kThreads) void k_rowscan(ShParams p)
 {
-    constexpr int kItems = 16;
+    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);   // wave-uniform
+    const int l = threadIdx.x & 63;
+    if (row >= p.nbk + p.P) return;
+    int32_t* a = row < p.nbk ? p.o.hist + (size_t)row * p.nb : p.o.thist + (size_t)(row - p.nbk) * p.nb;
     int carry = 0;
-    for (int base = 0; base < n; base += kItems * 1024) {
-        const int i0 = base + threadIdx.x * kItems;
-        int v[kItems];
-        if (i0 + kItems <= n) {
-#pragma unroll
-            for (int q = 0; q < kItems; q += 4) {
-                const int4 t = *(const int4*)(a + i0 + q);
-                v[q] = t.x;
-                v[q + 1] = t.y;
-                v[q + 2] = t.z;
-                v[q + 3] = t.w;
-            }
-        } else {
-#pragma unroll
-            for (int q = 0; q < kItems; ++q) v[q] = i0 + q < n ? a[i0 + q] : 0;
-        }
-        int sum = 0;
-#pragma unroll
-        for (int q = 0; q < kItems; ++q) sum += v[q];
-        int total;
-        int run = carry + block_excl_scan(sum, smem, &total);
-        int r = i0 % nb, f = i0 / nb;  // position of i0 + q within its run of nb
-#pragma unroll
-        for (int q = 0; q < kItems; ++q) {
-            if (i0 + q < n) {
-                a[i0 + q] = run;
-                if (r == 0) first[f] = run;
-            }
-            run += v[q];
-            if (++r == nb) {
-                r = 0;
-                ++f;
-            }
-        }
-        carry += total;
+    for (int base = 0; base < p.nb; base += 64) {
+        const int i = base + l;
+        const int v = i < p.nb ? a[i] : 0;
+        const int incl = wave_incl_scan(v);
+        if (i < p.nb) a[i] = carry + incl - v;
+        carry += __shfl(incl, 63);
     }
-    return carry;
+    if (l == 0) p.o.rowtot[row] = carry;
 }
 
 __global__ __launch_bounds__(1024) void k_scan(ShParams p)
@@ -116,17 +91,41 @@ __global__ __launch_bounds__(1024) void k_scan(ShParams p)
     __shared__ int smem[17];
     __shared__ int s_start[kMaxBuckets + 1];  // first offset of each bucket, then A
     __shared__ int s_tstart[65];              // first offset of each predicted group, then T
-    const int n = p.nbk * p.nb;
-    // hist -> global offsets; bucket b = s*P + g starts at hist[b*nb]
-    const int A = block_scan_inplace(p.o.hist, n, p.nb, s_start, smem);
-    const int T = block_scan_inplace(p.o.thist, p.P * p.nb, p.nb, s_tstart, smem);
+    const int nbk = p.nbk, P = p.P;
+    // bucket totals -> bucket starts (nbk <= 4096: four per thread)
+    int v[4], sum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int k = threadIdx.x * 4 + q;
+        v[q] = k < nbk ? p.o.rowtot[k] : 0;
+        sum += v[q];
+    }
+    int A;
+    int run = block_excl_scan(sum, smem, &A);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int k = threadIdx.x * 4 + q;
+        if (k < nbk) {
+            s_start[k] = run;
+            p.o.bstart[k] = run;
+        }
+        run += v[q];
+    }
     if (threadIdx.x == 0) {
-        s_start[p.nbk] = A;
-        s_tstart[p.P] = T;
+        s_start[nbk] = A;
+        p.o.bstart[nbk] = A;
+        int t = 0;
+        for (int g = 0; g < P; ++g) {
+            s_tstart[g] = t;
+            p.o.tstart[g] = t;
+            t += p.o.rowtot[nbk + g];
+        }
+        s_tstart[P] = t;
+        p.o.tstart[P] = t;
     }
     __syncthreads();
     auto bstart = [&](int bk) { return s_start[bk]; };
-    const int E = p.E, P = p.P, epg = E / P;
+    const int E = p.E, epg = E / P;
     for (int s = threadIdx.x; s <= E; s += 1024) {
         const int off = bstart(s * P);
         p.o.expert_off[s] = off;
@@ -174,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void k_scatter(ShParams p)
     __syncthreads();
     // counts -> starting positions: block offset + earlier waves' counts
     for (int i = threadIdx.x; i < nbk; i += kThreads) {
-        int run = p.o.hist[(size_t)i * p.nb + b];
+        int run = p.o.bstart[i] + p.o.hist[(size_t)i * p.nb + b];
         for (int q = 0; q < 4; ++q) {
             const int c = base[q][i];
             base[q][i] = run;
@@ -182,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void k_scatter(ShParams p)
         }
     }
     if (threadIdx.x < P) {
-        int run = p.o.thist[threadIdx.x * p.nb + b];
+        int run = p.o.tstart[threadIdx.x] + p.o.thist[threadIdx.x * p.nb + b];
         for (int q = 0; q < 4; ++q) {
             const int c = tbase[q][threadIdx.x];
             tbase[q][threadIdx.x] = run;
@@ -307,6 +306,7 @@ hipError_t launch_shuffle(const moe_cfg& c, int nb, int tpb, const int32_t* row_
     p.o = o;
     // the histogram kernel also runs for T == 0 so the table it writes is zero
     hipLaunchKernelGGL(k_hist, dim3(nb), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(k_rowscan, dim3(ceil_div(p.nbk + c.P, 4)), dim3(kThreads), 0, s, p);
     hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, p);
     if (c.T > 0) hipLaunchKernelGGL(k_scatter, dim3(nb), dim3(kThreads), 0, s, p);
     return hipGetLastError();
