@@ -84,3 +84,17 @@ def test_full_size(name):
 @pytest.mark.parametrize("name", DSV3)
 def test_full_size_dsv3(name):
     _check(_full_case(name))
+
+
+def test_max_tokens():
+    """The largest layer moe_validate accepts for the DeepSeek-V2-Lite shape:
+    T = 87381 tokens, whose A*H*2 = 2 147 469 312 bytes of sorted rows sit
+    just below the grouped GEMM's 2 GiB buffer-offset limit; same checks as
+    the full-size layers."""
+    from token_routing_shuffle_amd import moe
+    T = (2 ** 31 - 1) // (6 * 2048 * 2)
+    c = hn.make_case("dsv2lite", T=T, profile_tokens=65536)
+    assert moe.moe_validate(moe.make_cfg(c.cfg)) == moe.MOE_OK
+    assert moe.moe_validate(moe.make_cfg(c.cfg.replace(T=T + 1))) == moe.MOE_ESHAPE
+    _check(c)
+
