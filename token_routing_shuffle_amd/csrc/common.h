@@ -90,42 +90,32 @@ MOE_DEV float wave_max(float v)
                  fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
 }
 
-// Arg-best over the wave of (uk desc, id asc), carrying a payload s.
-MOE_DEV bool beats(uint32_t uk, uint32_t id, uint32_t ouk, uint32_t oid)
+// One DPP step of a 64-bit maximum: lanes the control gives no source keep
+// their value.  Row shifts 1, 2, 4, 8 leave each 16-lane row's maximum in its
+// lane 15; row_bcast:15 (rows 1 and 3) and row_bcast:31 (rows 2 and 3) carry
+// it to lane 63.
+template <int CTRL, int ROWMASK>
+MOE_DEV uint64_t dpp_max_u64(uint64_t v)
 {
-    return ouk > uk || (ouk == uk && oid < id);
+    const int lo = (int)(uint32_t)v, hi = (int)(uint32_t)(v >> 32);
+    const uint32_t olo = (uint32_t)__builtin_amdgcn_update_dpp(lo, lo, CTRL, ROWMASK, 0xF, false);
+    const uint32_t ohi = (uint32_t)__builtin_amdgcn_update_dpp(hi, hi, CTRL, ROWMASK, 0xF, false);
+    const uint64_t o = ((uint64_t)ohi << 32) | olo;
+    return o > v ? o : v;
 }
 
-template <int CTRL>
-MOE_DEV void argbest_step(uint32_t& uk, uint32_t& id, uint32_t& s)
+// Maximum of a 64-bit value over the wave, returned to every lane.  All 64
+// lanes must be active.
+MOE_DEV uint64_t wave_max_u64(uint64_t v)
 {
-    const uint32_t ouk = dpp_u32<CTRL>(uk), oid = dpp_u32<CTRL>(id), os = dpp_u32<CTRL>(s);
-    if (beats(uk, id, ouk, oid)) {
-        uk = ouk;
-        id = oid;
-        s = os;
-    }
-}
-
-MOE_DEV void wave_argbest(uint32_t& uk, uint32_t& id, uint32_t& s)
-{
-    argbest_step<0xB1>(uk, id, s);
-    argbest_step<0x4E>(uk, id, s);
-    argbest_step<0x141>(uk, id, s);
-    argbest_step<0x140>(uk, id, s);
-    uint32_t buk = readlane_u32(uk, 0), bid = readlane_u32(id, 0), bs = readlane_u32(s, 0);
-#pragma unroll
-    for (int r = 16; r < 64; r += 16) {
-        const uint32_t ouk = readlane_u32(uk, r), oid = readlane_u32(id, r);
-        if (beats(buk, bid, ouk, oid)) {
-            buk = ouk;
-            bid = oid;
-            bs = readlane_u32(s, r);
-        }
-    }
-    uk = buk;
-    id = bid;
-    s = bs;
+    v = dpp_max_u64<0x111, 0xF>(v);  // row_shr:1
+    v = dpp_max_u64<0x112, 0xF>(v);  // row_shr:2
+    v = dpp_max_u64<0x114, 0xF>(v);  // row_shr:4
+    v = dpp_max_u64<0x118, 0xF>(v);  // row_shr:8
+    v = dpp_max_u64<0x142, 0xA>(v);  // row_bcast:15
+    v = dpp_max_u64<0x143, 0xC>(v);  // row_bcast:31
+    const uint32_t lo = readlane_u32((uint32_t)v, 63), hi = readlane_u32((uint32_t)(v >> 32), 63);
+    return ((uint64_t)hi << 32) | lo;
 }
 
 MOE_DEV int wave_incl_scan(int v)

@@ -222,17 +222,6 @@ __global__ __launch_bounds__(256) void k_gate_logits(int T, int H, int E, int Kc
     }
 }
 
-// Winner of (ordered key desc, original id asc); sentinel uk = 0 loses to any key.
-MOE_DEV void better_take(uint32_t& uk, uint32_t& id, uint32_t& s, uint32_t ouk, uint32_t oid,
-                         uint32_t os)
-{
-    if (ouk > uk || (ouk == uk && oid < id)) {
-        uk = ouk;
-        id = oid;
-        s = os;
-    }
-}
-
 template <int NTW, bool BF16>
 __global__ __launch_bounds__(kThreads) void k_route(RouteParams p)
 {
@@ -480,22 +469,40 @@ __global__ __launch_bounds__(kThreads) void k_route(RouteParams p)
             for (int i = 0; i < NTW; ++i) ok[i] = ok[i] && ((kept >> (oid[i] / gsize)) & 1ull);
         }
 
-        bool taken[NTW];
+        // Candidates as one 64-bit key each: the ordered selection key above
+        // the complement of the original id, so a plain maximum is the
+        // (key desc, original id asc) winner; 0 marks no candidate (every
+        // real key's upper half is nonzero).  Each lane sorts its NTW keys
+        // descending; a round takes the wave maximum of the lanes' heads and
+        // the lane holding it drops its head.
+        uint64_t pk[NTW];
 #pragma unroll
-        for (int i = 0; i < NTW; ++i) taken[i] = false;
-        uint32_t myslot = 0;
+        for (int i = 0; i < NTW; ++i)
+            pk[i] = ok[i] ? ((uint64_t)ordered_key(key[i]) << 32) | (0xFFFFFFFFu - oid[i]) : 0ull;
+#pragma unroll
+        for (int a = 0; a < NTW; ++a)
+#pragma unroll
+            for (int b = NTW - 1; b > a; --b)
+                if (pk[b] > pk[b - 1]) {
+                    const uint64_t t = pk[b];
+                    pk[b] = pk[b - 1];
+                    pk[b - 1] = t;
+                }
+        uint64_t mine = 0;
         for (int j = 0; j < kt; ++j) {
-            uint32_t buk = 0, bid = 0xffffffffu, bs = 0;
+            const uint64_t best = wave_max_u64(pk[0]);
+            if (pk[0] == best) {
 #pragma unroll
-            for (int i = 0; i < NTW; ++i)
-                if (ok[i] && !taken[i]) better_take(buk, bid, bs, ordered_key(key[i]), oid[i], l + 64 * i);
-            wave_argbest(buk, bid, bs);
-#pragma unroll
-            for (int i = 0; i < NTW; ++i)
-                if (bs == (uint32_t)(l + 64 * i)) taken[i] = true;
-            if (l == j) myslot = bs;
+                for (int i = 0; i + 1 < NTW; ++i) pk[i] = pk[i + 1];
+                pk[NTW - 1] = 0ull;
+            }
+            if (l == j) mine = best;
         }
         if (kt == 0) continue;
+        // (a round with no candidate left — k above the candidates, which
+        // validation excludes — would yield 0: slot 0, as a guard)
+        const uint32_t mo = 0xFFFFFFFFu - (uint32_t)mine;
+        const uint32_t myslot = (l < kt && mine != 0ull && mo < (uint32_t)E) ? (uint32_t)s_o2s[mo] : 0u;
 
         const int base = s_rp[row];
         const float mylog = s_log[row][l < kt ? myslot : 0];
