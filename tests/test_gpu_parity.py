@@ -315,6 +315,12 @@ EDGE = {
     "one_token_id": ("qwen3", 700, dict(zipf_s=60.0)),
     # ragged k with many zero-k requests
     "prism_ragged_zeros": ("prism", 640, dict(k_choices=(0, 0, 8, 32))),
+    # tiled gate GEMM with E not a multiple of its 128-expert tile and T not
+    # of its 64-token tile (clamped rows, guarded stores), P = 3 groups
+    "gate_tiles_E192": ("qwen3", 300, dict(E=192, P=3)),
+    # tiled gate GEMM with the K split (few token tiles): 2 x 2 tiles of a
+    # 7168-wide gate, grouped sigmoid routing
+    "gate_ksplit": ("dsv3_decode", 100, {}),
 }
 
 
