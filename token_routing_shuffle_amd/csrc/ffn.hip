@@ -9,11 +9,13 @@
 //
 // One persistent kernel per GEMM walks a tile list covering the routed
 // segments [e_begin, e_end) and (optionally) the shared experts over all T
-// rows.  Tiles are ordered (segment, n-tile, m-tile) so the m-tiles that
-// share a weight tile are adjacent, and the list is cut into 8 contiguous
-// chunks of equal work, one per XCD (workgroup i runs on XCD i % 8), so weight
-// tiles are reused from that XCD's L2.  An XCD's workgroups claim its tiles
-// from a counter; once it is exhausted they claim from the other XCDs'.
+// rows.  Segments are grouped by the height of their m-tiles, tallest first,
+// and inside a segment tiles are ordered (n-tile, m-tile), so the m-tiles that
+// share a weight tile are adjacent.  Each height class is cut into 8 slices of
+// equal work, one per XCD (workgroup i runs on XCD i % 8), so weight tiles are
+// reused from that XCD's L2.  An XCD's workgroups claim the tiles of its
+// slices from a counter, tallest class first, so the tiles left at the end are
+// the shortest; once its slices are exhausted they claim from the other XCDs'.
 //
 // Tiles are 256 x BN (BN = 256, or 128 when N does not split into 256-wide
 // tiles); the last m-tile of a segment runs with the smallest height of 64,
@@ -183,12 +185,15 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
     constexpr int NPT = BN / 2;              // up: neurons per tile
     constexpr int kStageE = (BM + BN) * BK;  // bf16 elements per stage
     __shared__ __attribute__((aligned(16))) uint16_t smem[NS * kStageE];
-    __shared__ int s_pref[kMaxSeg + 1];   // tile index of each segment's first tile
-    __shared__ int s_wpref[kMaxSeg + 1];  // work before each segment
+    // segment lists in class-major order (position j holds segment s_seg[j])
+    __shared__ int s_seg[kMaxSeg];
+    __shared__ int s_pref[kMaxSeg + 1];   // tile index of each position's first tile
+    __shared__ int s_wpref[kMaxSeg + 1];  // work before each position
     __shared__ int s_row0[kMaxSeg];
     __shared__ int s_cnt[kMaxSeg];
     __shared__ int s_smem[17];
-    __shared__ int s_bound[9];  // chunk start of each XCD, then the tile count
+    __shared__ int s_cls[5];         // first position of each class, then nseg
+    __shared__ int s_bound[4 * 9];   // per class: slice start of each XCD, then its end
     __shared__ int s_tile;
 
     const int tid = threadIdx.x;
@@ -231,17 +236,62 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
     };
     {
         constexpr int SPT = (kMaxSeg + kThreads - 1) / kThreads;
-        int tiles[SPT], work[SPT], tsum = 0, wsum = 0;
+        // Segments in class-major order: class c holds the segments whose
+        // m-tiles are 256 - 64c rows high (empty segments go last), in
+        // segment order inside a class.  Ranks inside a class come from two
+        // scans of 16-bit counters packed in pairs.
+        int cls[SPT], pk01 = 0, pk23 = 0;
 #pragma unroll
         for (int q = 0; q < SPT; ++q) {
             const int i = tid * SPT + q;
-            tiles[q] = 0;
-            work[q] = 0;
+            cls[q] = 3;
             if (i < nseg) {
                 int row0, cnt, nt, kt;
                 seg_geom(i, row0, cnt, nt, kt);
-                s_row0[i] = row0;
-                s_cnt[i] = cnt;
+                if (cnt > 0) cls[q] = (BM - mtile_h(cnt)) / 64;
+                if (cls[q] < 2) pk01 += 1 << (16 * cls[q]);
+                else pk23 += 1 << (16 * (cls[q] - 2));
+            }
+        }
+        int t01, t23;
+        const int r01 = block_excl_scan(pk01, s_smem, &t01);
+        const int r23 = block_excl_scan(pk23, s_smem, &t23);
+        const int n0 = t01 & 0xFFFF, n1 = t01 >> 16, n2 = t23 & 0xFFFF;
+        int rk0 = r01 & 0xFFFF, rk1 = r01 >> 16, rk2 = (r23 & 0xFFFF) + n0 + n1, rk3 = (r23 >> 16) + n0 + n1 + n2;
+        rk1 += n0;
+#pragma unroll
+        for (int q = 0; q < SPT; ++q) {
+            const int i = tid * SPT + q;
+            if (i < nseg) {
+                const int c = cls[q];
+                s_seg[c == 0 ? rk0 : c == 1 ? rk1 : c == 2 ? rk2 : rk3] = i;
+                rk0 += c == 0;
+                rk1 += c == 1;
+                rk2 += c == 2;
+                rk3 += c == 3;
+            }
+        }
+        if (tid == 0) {
+            s_cls[0] = 0;
+            s_cls[1] = n0;
+            s_cls[2] = n0 + n1;
+            s_cls[3] = n0 + n1 + n2;
+            s_cls[4] = nseg;
+        }
+        __syncthreads();
+        // tile and work prefix sums over that order (position j holds
+        // segment s_seg[j])
+        int tiles[SPT], work[SPT], tsum = 0, wsum = 0;
+#pragma unroll
+        for (int q = 0; q < SPT; ++q) {
+            const int j = tid * SPT + q;
+            tiles[q] = 0;
+            work[q] = 0;
+            if (j < nseg) {
+                int row0, cnt, nt, kt;
+                seg_geom(s_seg[j], row0, cnt, nt, kt);
+                s_row0[j] = row0;
+                s_cnt[j] = cnt;
                 tiles[q] = ((cnt + BM - 1) / BM) * nt;
                 work[q] = cnt > 0 ? nt * ntile_work(cnt, kt) : 0;
             }
@@ -253,10 +303,10 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
         int wrun = block_excl_scan(wsum, s_smem, &wtot);
 #pragma unroll
         for (int q = 0; q < SPT; ++q) {
-            const int i = tid * SPT + q;
-            if (i < nseg) {
-                s_pref[i] = trun;
-                s_wpref[i] = wrun;
+            const int j = tid * SPT + q;
+            if (j < nseg) {
+                s_pref[j] = trun;
+                s_wpref[j] = wrun;
             }
             trun += tiles[q];
             wrun += work[q];
@@ -266,25 +316,29 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
             s_wpref[nseg] = wtot;
         }
         __syncthreads();
-        // Chunk starts of the eight XCDs: XCD x owns the tiles whose work
-        // starts in [total * x / 8, total * (x + 1) / 8).  Workgroup i runs
-        // on XCD i % 8; the XCD's workgroups take its tiles from its counter
-        // (tiles differ in length, so a static split would leave some
-        // workgroups idle at the end).  A workgroup whose XCD has run out
-        // continues on the next XCDs' counters.  The up projection walks each
-        // chunk from its end, the down projection from its start (each order
-        // measured the faster one for that GEMM).
-        if (tid < 9) {
-            const long long target = ((long long)wtot * tid) >> 3;
-            int b = ttot;
-            if (target < wtot) {
-                int lo = 0, hi = nseg - 1;
+        // Each class's tiles are cut into eight slices of equal work, one per
+        // XCD: XCD x owns the class-c tiles whose work starts in
+        // [W * x / 8, W * (x + 1) / 8) of that class's work W.  Workgroup i
+        // runs on XCD i % 8; the XCD's workgroups take tiles from its counter,
+        // through its slices of classes 0, 1, 2, 3 in turn (tiles differ in
+        // length, so a static split would leave some workgroups idle at the
+        // end, and with the tallest tiles first the last ones claimed are the
+        // shortest).  A workgroup whose XCD has run out continues on the
+        // next XCDs' counters.
+        if (tid < 36) {
+            const int c = tid / 9, x = tid % 9;
+            const int ps = s_cls[c], pe = s_cls[c + 1];
+            const int w0 = s_wpref[ps], w1 = s_wpref[pe];
+            const long long target = w0 + (((long long)(w1 - w0) * x) >> 3);
+            int b = s_pref[pe];
+            if (target < w1) {
+                int lo = ps, hi = pe - 1;
                 while (lo < hi) {
                     const int mid = (lo + hi + 1) >> 1;
                     if (s_wpref[mid] <= target) lo = mid; else hi = mid - 1;
                 }
                 int row0, cnt, nt, kt;
-                seg_geom(lo, row0, cnt, nt, kt);
+                seg_geom(s_seg[lo], row0, cnt, nt, kt);
                 const int mt = (cnt + BM - 1) / BM;
                 const int wn_ = ntile_work(cnt, kt);
                 const int rem = (int)(target - s_wpref[lo]);
@@ -297,13 +351,19 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
         __syncthreads();
     }
     // tile claims (thread 0): the tile for counter value v of XCD
-    // (xcd + src) & 7, else the next XCDs'; -1 when all are done
+    // (xcd + src) & 7, through its four class slices; else the next XCDs';
+    // -1 when all are done
     int src = 0;
     auto claim = [&]() -> int {
         for (;;) {
             const int y = (xcd + src) & 7;
-            const int v = atomicAdd(&p.ctr[y], 1);
-            if (v < s_bound[y + 1] - s_bound[y]) return UP ? s_bound[y + 1] - 1 - v : s_bound[y] + v;
+            int v = atomicAdd(&p.ctr[y], 1);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int b0 = s_bound[c * 9 + y], len = s_bound[c * 9 + y + 1] - b0;
+                if (v < len) return b0 + v;
+                v -= len;
+            }
             if (++src == 8) return -1;
         }
     };
@@ -320,12 +380,13 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
             if (s_pref[mid] <= L) lo = mid; else hi = mid - 1;
         }
         // tile values are wave-uniform: keep them in scalar registers
-        const int seg = __builtin_amdgcn_readfirstlane(lo);
+        const int pos = __builtin_amdgcn_readfirstlane(lo);
+        const int seg = __builtin_amdgcn_readfirstlane(s_seg[pos]);
         const bool shared = seg >= p.n_routed;
-        const int row0 = __builtin_amdgcn_readfirstlane(s_row0[seg]);
-        const int cnt = __builtin_amdgcn_readfirstlane(s_cnt[seg]);
+        const int row0 = __builtin_amdgcn_readfirstlane(s_row0[pos]);
+        const int cnt = __builtin_amdgcn_readfirstlane(s_cnt[pos]);
         const int mt = (cnt + BM - 1) / BM;
-        const int local = L - __builtin_amdgcn_readfirstlane(s_pref[seg]);
+        const int local = L - __builtin_amdgcn_readfirstlane(s_pref[pos]);
         const int hgt = mtile_h(cnt);
         const int ntile = local / mt, m0 = (local % mt) * hgt;
         const int K = shared ? p.shK : p.K;
