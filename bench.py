@@ -164,8 +164,9 @@ def main():
         if args.fuse_gather == 0 else None,
     }
 
-    srs_sag = share = cosched = None
+    srs_sag = share = cosched = dispatch = None
     if not args.no_extras:
+        dispatch = time_dispatch(cfg, c, d, x, tok, row_ptr, topk_slot, ws, A, args, torch, moe, dev)
         srs_sag = time_srs_sag(cfg, c, tables, args, torch, np, moe, wl, dev)
         share = group_share(cfg, c, d, x, tok, row_ptr, topk_slot, ws, args, torch, np, moe, dev)
         cosched = coschedule(cfg, c, tables, prof, tok, row_ptr, topk_slot, d["lut"], torch, np, moe,
@@ -201,12 +202,57 @@ def main():
                          % (n_bd, up_timed_ms),
         "secondary": secondary,
         "roofline": roofline,
+        "dispatch": dispatch,
         "srs_sag": srs_sag,
         "group_share": share,
         "coschedule": cosched,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+def time_dispatch(cfg, c, d, x, tok, row_ptr, topk_slot, ws, A, args, torch, moe, dev):
+    """The dispatch stage as a call of its own (moe_shuffle: LUT lookup,
+    counting sort and the gather of x into expert-contiguous rows) on the
+    layer's routing, timed with one event pair around many calls; the same
+    call without the gather gives the metadata part, the difference the
+    gather kernel.  HBM roofline of the whole stage (x read once, A rows
+    written, index metadata) and of the gather alone (T + A rows)."""
+    T, H, E, P = cfg.T, cfg.H, cfg.E, cfg.P
+    b = 2 if cfg.dtype == "bf16" else 4
+    A_max = T * cfg.k
+    i32 = dict(dtype=torch.int32, device=dev)
+    o = [torch.empty(k, **i32) for k in (E, E + 1, P, P + 1, P * P, T, P + 1, A_max, A_max)]
+    xs = torch.empty((A_max, H), dtype=x.dtype, device=dev)
+    reps = max(10, min(args.steps, 100))
+
+    def timed(dst):
+        def call():
+            moe.moe_shuffle(c, row_ptr, topk_slot, tok, d["lut"], x, *o, dst, ws)
+        for _ in range(5):
+            call()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(reps):
+            call()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps
+
+    full_ms = timed(xs)
+    meta_ms = timed(None)
+    gather_ms = max(full_ms - meta_ms, 1e-6)
+    nbytes = T * H * b + A * H * b + 8.0 * T + 12.0 * A
+    gbytes = T * H * b + A * H * b
+    gbs, ggbs = nbytes / (full_ms * 1e-3) / 1e9, gbytes / (gather_ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes_per_launch": nbytes,
+            "avg_launch_ms": round(full_ms, 4), "metadata_ms": round(meta_ms, 4),
+            "gather": {"achieved": round(ggbs, 1), "frac": round(ggbs / HBM_PEAK_GBS, 4),
+                       "bytes_per_launch": gbytes, "ms": round(gather_ms, 4)},
+            "reps": reps,
+            "note": "moe_shuffle with and without x_sorted, back to back; the layer step fuses "
+                    "the gather into GEMM1's row loads"}
 
 
 def time_srs_sag(cfg, c, tables, args, torch, np, moe, wl, dev):
