@@ -408,13 +408,14 @@ def test_ffn_group_share_matches_full():
 
 @pytest.mark.parametrize("name", ["dsv2lite_1000", "prism_1000"])
 def test_ffn_every_tile_height(name):
-    """Expert row counts chosen so that the last m-tile of a segment takes
-    each tile height (64, 128, 192, 256 rows) and the edges around them; the
-    GEMMs are checked row by row against the oracle's expert FFN."""
+    """Expert row counts chosen so that the m-tiles of a segment take each
+    tile height (32, 64, ..., 256 rows) and the edges around them; the GEMMs
+    are checked row by row against the oracle's expert FFN."""
     c = case(name)
     m = moe_mod()
     E, H = c.cfg.E, c.cfg.H
-    counts = [1, 63, 64, 65, 127, 128, 129, 191, 192, 193, 255, 256, 257, 300, 0, 511, 513]
+    counts = [1, 63, 64, 65, 127, 128, 129, 191, 192, 193, 255, 256, 257, 300, 0, 511, 513,
+              31, 32, 33, 95, 96, 97, 159, 160, 161, 223, 224, 225, 383, 449, 700]
     counts = (counts + [0] * E)[:E]
     off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     A = int(off[-1])

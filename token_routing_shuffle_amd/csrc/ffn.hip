@@ -18,9 +18,9 @@
 // the shortest; once its slices are exhausted they claim from the other XCDs'.
 //
 // Tiles are 256 x BN (BN = 256, or 128 when N does not split into 256-wide
-// tiles); the last m-tile of a segment runs with the smallest height of 64,
-// 128, 192 or 256 rows that covers its rows, so at most 63 rows of MFMA work
-// are padding.  Eight waves in a 2 x 4 grid each own a (BM/2) x (BN/4) block:
+// tiles); a segment's m-tiles all have the height (a multiple of 32 rows,
+// at most 256) that covers its rows in the fewest tiles, so less than 32
+// rows per m-tile of MFMA work are padding.  Eight waves in a 2 x 4 grid each own a (BM/2) x (BN/4) block:
 // at 256 x 256 that is 128 x 64 per wave, 8 x 4 MFMA 16x16x32 bf16 blocks
 // with 128 fp32 accumulators per lane, two waves per SIMD.  The 256 x 256
 // tile fetches 2/3 of the L2 bytes per flop of a 128 x 256 tile.
@@ -219,11 +219,11 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
         }
     };
     // A segment of cnt rows is cut into mt = ceil(cnt / 256) m-tiles of
-    // equal height (a multiple of 64 rows): the tiles that share a weight tile
+    // equal height (a multiple of 32 rows): the tiles that share a weight tile
     // then run at the same speed, so the second reader finds it in L2.
     auto mtile_h = [&](int cnt) {
         const int mt = (cnt + BM - 1) / BM;
-        return ((cnt + mt - 1) / mt + 63) / 64 * 64;
+        return ((cnt + mt - 1) / mt + 31) / 32 * 32;
     };
     // Work of one k-step of an m-tile of height h, in units fitted to the
     // measured k-step times of 192- and 256-row tiles (about 0.8 : 1): the
@@ -237,8 +237,8 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
     {
         constexpr int SPT = (kMaxSeg + kThreads - 1) / kThreads;
         // Segments in class-major order: class c holds the segments whose
-        // m-tiles are 256 - 64c rows high (empty segments go last), in
-        // segment order inside a class.  Ranks inside a class come from two
+        // m-tiles are 256 - 64c or 224 - 64c rows high (empty segments go
+        // last), in segment order inside a class.  Ranks inside a class come from two
         // scans of 16-bit counters packed in pairs.
         int cls[SPT], pk01 = 0, pk23 = 0;
 #pragma unroll
@@ -414,14 +414,17 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
         const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc((void*)Bseg, (short)0, b_bytes, 0x00020000);
         const int KT = K / BK;
 
-        // RT = 16-row blocks per wave: the tile has 32 * RT rows (RT = 8, 6,
-        // 4 or 2), split between the two wave rows.
+        // RT = 16-row blocks per wave: the tile has 32 * RT rows (RT = 1..8),
+        // split between the two wave rows.  The DMA loads the A rows in
+        // groups of 64 (kAload), so for odd RT the last 32 rows loaded are
+        // not used by the MFMAs.
         auto run_tile = [&](auto rt_tag) {
             constexpr int RT = decltype(rt_tag)::value;
-            constexpr int kArows = RT * 32;                  // A rows loaded
-            constexpr int NA = kArows / 8;                   // A DMA instructions
-            constexpr int NI = (kArows + BN) / 8 / NW;       // DMA instructions per wave
-            static_assert((kArows + BN) % 32 == 0, "stage split");
+            constexpr int kArows = RT * 32;                  // A rows of the tile
+            constexpr int kAload = (RT + 1) / 2 * 64;        // A rows loaded
+            constexpr int NA = kAload / 8;                   // A DMA instructions
+            constexpr int NI = (kAload + BN) / 8 / NW;       // DMA instructions per wave
+            static_assert((kAload + BN) % 64 == 0, "stage split");
             // DMA instruction q = w*NI + jj covers 8 LDS rows; lane l fills
             // row (l >> 3) of them at position l & 7, which holds the row's
             // global chunk swz(row, l & 7) (the swizzle is an involution).
@@ -574,7 +577,7 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
                 }
                 __syncthreads();
 #pragma unroll
-                for (int qq = 0; qq < (kArows * CPR) / kThreads; ++qq) {
+                for (int qq = 0; qq < (kArows * CPR + kThreads - 1) / kThreads; ++qq) {
                     const int idx = tid + qq * kThreads;
                     const int row = idx / CPR, ch = idx % CPR;
                     int col;
@@ -592,10 +595,14 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
                 __syncthreads();
             }
         };
-        if (hgt > 192) run_tile(IntC<8>{});
-        else if (hgt > 128) run_tile(IntC<6>{});
-        else if (hgt > 64) run_tile(IntC<4>{});
-        else run_tile(IntC<2>{});
+        if (hgt > 224) run_tile(IntC<8>{});
+        else if (hgt > 192) run_tile(IntC<7>{});
+        else if (hgt > 160) run_tile(IntC<6>{});
+        else if (hgt > 128) run_tile(IntC<5>{});
+        else if (hgt > 96) run_tile(IntC<4>{});
+        else if (hgt > 64) run_tile(IntC<3>{});
+        else if (hgt > 32) run_tile(IntC<2>{});
+        else run_tile(IntC<1>{});
     }
 }
 
