@@ -163,6 +163,7 @@ def main():
                               ((stage_ms["shuffle"] + stage_ms["gather"]) * 1e-3) / 1e9, 1)
         if args.fuse_gather == 0 else None,
     }
+    stage_roofline = stage_rooflines(cfg, A, alg, stage_ms, up_ms)
 
     srs_sag = share = cosched = dispatch = None
     if not args.no_extras:
@@ -201,6 +202,7 @@ def main():
                          "(each event pair adds GPU time; ffn_up in the timed steps: %.4f ms)"
                          % (n_bd, up_timed_ms),
         "secondary": secondary,
+        "stage_roofline": stage_roofline,
         "roofline": roofline,
         "dispatch": dispatch,
         "srs_sag": srs_sag,
@@ -209,6 +211,43 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+MALL_BYTES = 256 << 20
+
+
+def stage_rooflines(cfg, A, alg, stage_ms, up_timed_ms):
+    """Every stage of the layer step against its roofline: algorithmic bytes
+    (HBM, 8 TB/s) or flops (dense bf16 MFMA, 2.5 PFLOP/s) over the stage's
+    event-timed duration from the breakdown pass (GEMM1: the timed steps).
+    The route stage is given both ways (its gate GEMM is a contraction, its
+    bytes are the x read).  "mall_resident" marks stages whose bytes fit in
+    the 256 MB Infinity Cache, where the HBM fraction can exceed what HBM
+    alone would allow.  Each event pair adds a few microseconds to short
+    stages."""
+    T, H, E = cfg.T, cfg.H, cfg.E
+    b = 2 if cfg.dtype == "bf16" else 4
+
+    def hbm(nbytes, ms):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved_gbs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                "bytes": float(nbytes), "ms": round(ms, 4), "mall_resident": nbytes <= MALL_BYTES}
+
+    def mfma(flops, ms):
+        tf = flops / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved_tflops": round(tf, 2),
+                "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4), "flops": float(flops), "ms": round(ms, 4)}
+
+    route_bytes = T * H * b + E * H * b + 8.0 * A + 4.0 * (T + 1) + 4.0 * T
+    r = hbm(route_bytes, stage_ms["route"])
+    r["mfma_frac"] = mfma(2.0 * T * H * E, stage_ms["route"])["frac"]
+    return {
+        "route": r,
+        "shuffle_metadata": hbm(8.0 * T + 12.0 * A, stage_ms["shuffle"]),
+        "ffn_up": mfma(alg["ffn_up_flops"], up_timed_ms),
+        "ffn_down": mfma(alg["ffn_down_flops"], stage_ms["ffn_down"]),
+        "combine": hbm(alg["combine_bytes"], stage_ms["combine"]),
+    }
 
 
 def time_dispatch(cfg, c, d, x, tok, row_ptr, topk_slot, ws, A, args, torch, moe, dev):
@@ -250,7 +289,7 @@ def time_dispatch(cfg, c, d, x, tok, row_ptr, topk_slot, ws, A, args, torch, moe
             "avg_launch_ms": round(full_ms, 4), "metadata_ms": round(meta_ms, 4),
             "gather": {"achieved": round(ggbs, 1), "frac": round(ggbs / HBM_PEAK_GBS, 4),
                        "bytes_per_launch": gbytes, "ms": round(gather_ms, 4)},
-            "reps": reps,
+            "reps": reps, "mall_resident": nbytes <= MALL_BYTES,
             "note": "moe_shuffle with and without x_sorted, back to back; the layer step fuses "
                     "the gather into GEMM1's row loads"}
 
