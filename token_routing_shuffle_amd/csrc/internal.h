@@ -14,7 +14,15 @@ namespace moe {
 // count table costing the single-block scan more than the shorter blocks
 // gained.)
 constexpr int kShuffleMaxTPB = 256;
-inline int shuffle_tpb(int, int, int) { return kShuffleMaxTPB; }
+// Tokens per counting-sort block: 256, halved (down to 64) while the layer
+// would get fewer than 128 blocks, so that mid-sized layers still spread the
+// histogram and scatter over many CUs.
+inline int shuffle_tpb(int T, int, int)
+{
+    int tpb = kShuffleMaxTPB;
+    while (tpb > 64 && (T + tpb - 1) / tpb < 128) tpb /= 2;
+    return tpb;
+}
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 inline int ilog2(int v) { int r = 0; while ((1 << r) < v) ++r; return r; }
