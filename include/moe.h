@@ -326,6 +326,18 @@ int32_t moe_optimize_placement(const moe_cfg* cfg, int32_t n_tok, const int32_t*
 int32_t moe_request_group_hist(const moe_cfg* cfg, int32_t n_req, const int32_t* req_ptr,
                                const int32_t* tok, const int32_t* lut, int32_t* hist, void* stream);
 
+/* The sigmoid of the grouped gate's selection keys, on its own: y[i] =
+ * 1 / (1 + exp(-x[i])) in fp32 with exp evaluated as in moe_route (Cody-Waite
+ * reduction, degree-7 Taylor polynomial in fused multiply-adds, exact
+ * scaling; 0 below -87, +inf above 88), each step one IEEE-rounded fp32
+ * operation, so any other implementation of the same steps reproduces it bit
+ * for bit.  The selection of the sigmoid gate compares these values, which is
+ * why they are exported for checking (DeepSeek-V3-style gating is what the
+ * Sem-MoE pages evaluate on; they do not describe the gate itself).
+ *   x[n], y[n]  device fp32 arrays (y may equal x); n >= 0.
+ * MOE_EINVAL for n < 0 or a NULL pointer with n > 0. */
+int32_t moe_sigmoid(const float* x, float* y, int64_t n, void* stream);
+
 /* Device tensors of one layer for moe_forward (host struct of device pointers). */
 typedef struct moe_weights {
     const void* Wg;              /* [E,H] slot order */

@@ -32,7 +32,8 @@ def test_header_declares_the_boundary():
         "moe_sag", "moe_shuffle", "moe_srs", "moe_validate", "moe_workspace_bytes",
         "moe_route_workspace_bytes",
         "moe_token_group_counts", "moe_lut_from_counts", "moe_expert_group_counts",
-        "moe_balanced_assign", "moe_optimize_placement", "moe_request_group_hist"])
+        "moe_balanced_assign", "moe_optimize_placement", "moe_request_group_hist",
+        "moe_sigmoid"])
 
 
 def test_library_exports_every_declared_symbol(m):
@@ -141,6 +142,9 @@ def test_calls_reject_null_pointers_before_launching(m):
     assert L.moe_combine(ref, *([None] * 7)) == m.MOE_EINVAL
     w, i = m.moe_weights(), m.moe_inputs()
     assert L.moe_forward(ref, ctypes.byref(w), ctypes.byref(i), None, None, None, 0, None) == m.MOE_EINVAL
+    assert L.moe_sigmoid(None, None, 10, None) == m.MOE_EINVAL
+    assert L.moe_sigmoid(None, None, -1, None) == m.MOE_EINVAL
+    assert L.moe_sigmoid(None, None, 0, None) == m.MOE_OK
 
 
 def test_calls_reject_small_or_misaligned_workspace(m):

@@ -568,6 +568,16 @@ MOE_API int32_t moe_request_group_hist(const moe_cfg* cfg, int32_t n_req, const 
     return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_request_group_hist");
 }
 
+MOE_API int32_t moe_sigmoid(const float* x, float* y, int64_t n, void* stream)
+{
+    if (n < 0) return fail(MOE_EINVAL, "n < 0");
+    if (n == 0) return MOE_OK;
+    REQUIRE(x);
+    REQUIRE(y);
+    hipError_t e = launch_sigmoid(x, y, n, (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_sigmoid");
+}
+
 MOE_API int32_t moe_forward(const moe_cfg* cfg, const moe_weights* w, const moe_inputs* in,
                             void* out, const moe_exports* ex, void* ws, size_t ws_bytes,
                             void* stream)

@@ -62,6 +62,7 @@ struct ShuffleOut {
     int32_t *rowtot, *bstart, *tstart;  // row totals, bucket and group starts (scratch)
     int32_t* gemm_ctr;  // [16] grouped-GEMM tile counters to zero, or nullptr
 };
+hipError_t launch_sigmoid(const float* x, float* y, int64_t n, hipStream_t s);
 hipError_t launch_shuffle(const moe_cfg& c, int nb, int tpb, const int32_t* row_ptr,
                           const int32_t* topk_slot, const int32_t* tok, const int32_t* lut,
                           const ShuffleOut& o, hipStream_t s);

@@ -564,6 +564,24 @@ hipError_t launch_route_t(const RouteParams& p, hipStream_t s)
 
 }  // namespace
 
+namespace {
+// y[i] = the selection sigmoid of x[i] (cw_sigmoidf, the same code the route
+// kernel runs), grid-stride.
+__global__ __launch_bounds__(256) void k_sigmoid(const float* __restrict__ x, float* __restrict__ y, int64_t n)
+{
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) y[i] = cw_sigmoidf(x[i]);
+}
+}  // namespace
+
+hipError_t launch_sigmoid(const float* x, float* y, int64_t n, hipStream_t s)
+{
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = std::min<int64_t>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(k_sigmoid, dim3((unsigned)blocks), dim3(256), 0, s, x, y, n);
+    return hipGetLastError();
+}
+
 hipError_t launch_row_ptr(const moe_cfg& c, const int32_t* k_tok, int32_t* row_ptr, hipStream_t s)
 {
     // with a fixed k and T > 0 the route kernel writes row_ptr itself

@@ -108,6 +108,8 @@ def _load():
     lib.moe_forward.restype = i32
     lib.moe_forward.argtypes = [P(moe_cfg), P(moe_weights), P(moe_inputs), vp, P(moe_exports),
                                 vp, sz, vp]
+    lib.moe_sigmoid.restype = i32
+    lib.moe_sigmoid.argtypes = [vp, vp, ctypes.c_int64, vp]
     return lib
 
 
@@ -125,7 +127,8 @@ EXPORTED = ("moe_validate", "moe_workspace_bytes", "moe_route_workspace_bytes", 
             "moe_route", "moe_shuffle",
             "moe_expert_ffn", "moe_combine", "moe_forward", "moe_srs", "moe_sag",
             "moe_token_group_counts", "moe_lut_from_counts", "moe_expert_group_counts",
-            "moe_balanced_assign", "moe_optimize_placement", "moe_request_group_hist")
+            "moe_balanced_assign", "moe_optimize_placement", "moe_request_group_hist",
+            "moe_sigmoid")
 
 
 def _p(t) -> Optional[int]:
@@ -300,6 +303,13 @@ def moe_request_group_hist(cfg, n_req, req_ptr, tok, lut, hist, stream=None):
     rc = lib().moe_request_group_hist(ctypes.byref(cfg), int(n_req), _p(req_ptr), _p(tok), _p(lut),
                                       _p(hist), _stream(stream))
     _check(rc, "moe_request_group_hist")
+
+
+def moe_sigmoid(x, y, n=None, stream=None):
+    """y[:n] = the selection sigmoid of x[:n] (fp32 device tensors)."""
+    n = x.numel() if n is None else int(n)
+    rc = lib().moe_sigmoid(_p(x), _p(y), n, _stream(stream))
+    _check(rc, "moe_sigmoid")
 
 
 def moe_forward(cfg, weights: moe_weights, inputs: moe_inputs, out, exports=None, ws=None,
