@@ -153,7 +153,7 @@ def main():
     roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
                 "traffic": traffic, "traffic_unit": "bytes per launch", "traffic_source": traffic_note,
-                "kernel": "k_grouped_gemm<true,256> (GEMM1 + SwiGLU, routed + shared)",
+                "kernel": "k_grouped_gemm<true,256,256> (GEMM1 + SwiGLU, routed + shared)",
                 "flops_per_launch": alg["ffn_up_flops"], "avg_launch_ms": round(up_ms, 4)}
     secondary = {
         "ffn_down_tflops": round(alg["ffn_down_flops"] / (stage_ms["ffn_down"] * 1e-3) / 1e12, 2),

@@ -409,8 +409,10 @@ def test_ffn_group_share_matches_full():
 @pytest.mark.parametrize("name", ["dsv2lite_1000", "prism_1000"])
 def test_ffn_every_tile_height(name):
     """Expert row counts chosen so that the m-tiles of a segment take each
-    tile height (32, 64, ..., 256 rows) and the edges around them; the GEMMs
-    are checked row by row against the oracle's expert FFN."""
+    tile height (32, 64, ..., 256 rows of the 256 x 256 tiles; 64, ..., 384
+    rows of the 384 x 128 tiles the MoE-Prism shape's GEMM1 runs) and the
+    edges around them; the GEMMs are checked row by row against the oracle's
+    expert FFN."""
     c = case(name)
     m = moe_mod()
     E, H = c.cfg.E, c.cfg.H

@@ -17,12 +17,13 @@
 // slices from a counter, tallest class first, so the tiles left at the end are
 // the shortest; once its slices are exhausted they claim from the other XCDs'.
 //
-// Tiles are 256 x BN (BN = 256, or 128 when N does not split into 256-wide
-// tiles); a segment's m-tiles all have the height (a multiple of 32 rows,
-// at most 256) that covers its rows in the fewest tiles, so less than 32
-// rows per m-tile of MFMA work are padding.  Eight waves in a 2 x 4 grid each own a (BM/2) x (BN/4) block:
-// at 256 x 256 that is 128 x 64 per wave, 8 x 4 MFMA 16x16x32 bf16 blocks
-// with 128 fp32 accumulators per lane, two waves per SIMD.  The 256 x 256
+// Tiles are 256 x 256, or 384 x 128 when N does not split into 256-wide
+// tiles; a segment's m-tiles all have the height (a multiple of 32 rows, or
+// of 64 for the 384-row tiles) that covers its rows in the fewest tiles, so
+// little MFMA work is padding.  Eight waves: at 256 x 256 a 2 x 4 grid of
+// 128 x 64 blocks per wave, 8 x 4 MFMA 16x16x32 bf16 blocks with 128 fp32
+// accumulators per lane; at 384 x 128 a 4 x 2 grid of 96 x 64 blocks (96
+// accumulators); two waves per SIMD.  The 256 x 256
 // tile fetches 2/3 of the L2 bytes per flop of a 128 x 256 tile.
 //
 // Operands go HBM/L2 -> LDS directly (buffer_load_dwordx4 ... lds): no
@@ -47,7 +48,7 @@ namespace moe {
 namespace {
 
 constexpr int BM = 256, BK = 64, NS = 2;
-// waves along N (the wave grid is 2 x kWavesN)
+// waves along N of the 256 x 256 tiles (the wave grid is 2 x kWavesN)
 constexpr int kWavesN = 4;
 constexpr int kMaxSeg = 516;
 
@@ -176,12 +177,17 @@ MOE_DEV void frag_wait(bf16x8_t (&a)[NA], bf16x8_t (&b)[NB])
 #endif
 }
 
-template <bool UP, int BN>
-__global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
+template <bool UP, int BN, int BMT>
+__global__ __launch_bounds__(512, 1) void k_grouped_gemm(GemmParams p)
 {
-    constexpr int NW = 2 * kWavesN;          // waves
+    // tile rows at most: 256 (waves 2 x 4), or 384 with BN = 128 (waves 4 x 2)
+    constexpr int BM = BMT;
+    constexpr int kWN = BMT == 384 ? 2 : kWavesN;   // waves along N
+    constexpr int kWM = 8 / kWN;                    // waves along M
+    constexpr int kHq = kWM * 16;                   // tile height granularity
+    constexpr int NW = kWM * kWN;            // waves
     constexpr int kThreads = 64 * NW;
-    constexpr int WC = BN / (16 * kWavesN);  // 16-column blocks per wave
+    constexpr int WC = BN / (16 * kWN);      // 16-column blocks per wave
     constexpr int NPT = BN / 2;              // up: neurons per tile
     constexpr int kStageE = (BM + BN) * BK;  // bf16 elements per stage
     __shared__ __attribute__((aligned(16))) uint16_t smem[NS * kStageE];
@@ -198,7 +204,7 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
 
     const int tid = threadIdx.x;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
-    const int wm = w / kWavesN, wn = w % kWavesN;
+    const int wm = w / kWN, wn = w % kWN;
     const int nseg = p.n_routed + p.has_shared;
     const int xcd = blockIdx.x & 7;
 
@@ -223,7 +229,7 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
     // then run at the same speed, so the second reader finds it in L2.
     auto mtile_h = [&](int cnt) {
         const int mt = (cnt + BM - 1) / BM;
-        return ((cnt + mt - 1) / mt + 31) / 32 * 32;
+        return ((cnt + mt - 1) / mt + kHq - 1) / kHq * kHq;
     };
     // Work of one k-step of an m-tile of height h, in units fitted to the
     // measured k-step times of 192- and 256-row tiles (about 0.8 : 1): the
@@ -248,7 +254,7 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
             if (i < nseg) {
                 int row0, cnt, nt, kt;
                 seg_geom(i, row0, cnt, nt, kt);
-                if (cnt > 0) cls[q] = (BM - mtile_h(cnt)) / 64;
+                if (cnt > 0) cls[q] = min(3, (BM - mtile_h(cnt)) / (BM / 4));
                 if (cls[q] < 2) pk01 += 1 << (16 * cls[q]);
                 else pk23 += 1 << (16 * (cls[q] - 2));
             }
@@ -420,8 +426,8 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
         // not used by the MFMAs.
         auto run_tile = [&](auto rt_tag) {
             constexpr int RT = decltype(rt_tag)::value;
-            constexpr int kArows = RT * 32;                  // A rows of the tile
-            constexpr int kAload = (RT + 1) / 2 * 64;        // A rows loaded
+            constexpr int kArows = RT * kHq;                 // A rows of the tile
+            constexpr int kAload = (kArows + 63) / 64 * 64;  // A rows loaded
             constexpr int NA = kAload / 8;                   // A DMA instructions
             constexpr int NI = (kAload + BN) / 8 / NW;       // DMA instructions per wave
             static_assert((kAload + BN) % 64 == 0, "stage split");
@@ -487,7 +493,7 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
             bf16x8_t af0[RT], bf0[WC], af1[RT], bf1[WC];
             const int lrow = lane & 15;
             const uint32_t a_row = lds_addr(smem) + (wm * (RT * 16) + lrow) * (BK * 2);
-            const uint32_t b_row = lds_addr(smem) + (BM + wn * (UP ? NPT / kWavesN : BN / kWavesN) + lrow) * (BK * 2);
+            const uint32_t b_row = lds_addr(smem) + (BM + wn * (UP ? NPT / kWN : BN / kWN) + lrow) * (BK * 2);
             const uint32_t c0 = swz(lrow, lane >> 4) << 4, c1 = swz(lrow, 4 + (lane >> 4)) << 4;
             const uint32_t a_base[2] = {a_row + c0, a_row + c1};
             const uint32_t b_base[2] = {b_row + c0, b_row + c1};
@@ -559,7 +565,7 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
                             uint2 v;
                             v.x = pack2_bf16(silu_fast(g[0]) * u[0], silu_fast(g[1]) * u[1]);
                             v.y = pack2_bf16(silu_fast(g[2]) * u[2], silu_fast(g[3]) * u[3]);
-                            *(uint2*)&Cs[row * CS + wn * (NPT / kWavesN) + c * 16 + (l >> 4) * 4] = v;
+                            *(uint2*)&Cs[row * CS + wn * (NPT / kWN) + c * 16 + (l >> 4) * 4] = v;
                         }
                 } else {
 #pragma unroll
@@ -572,7 +578,7 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
                             uint2 v;
                             v.x = pack2_bf16(a[0], a[1]);
                             v.y = pack2_bf16(a[2], a[3]);
-                            *(uint2*)&Cs[row * CS + wn * (BN / (2 * kWavesN)) + c * 16 + (l >> 4) * 4] = v;
+                            *(uint2*)&Cs[row * CS + wn * (BN / (2 * kWN)) + c * 16 + (l >> 4) * 4] = v;
                         }
                 }
                 __syncthreads();
@@ -584,9 +590,9 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
                     if (UP) {
                         col = ntile * NPT + ch * 8;
                     } else {
-                        constexpr int WPP = BN / (2 * kWavesN);  // columns per wave per pass
+                        constexpr int WPP = BN / (2 * kWN);  // columns per wave per pass
                         const int lc = ch * 8, wv = lc / WPP;
-                        col = ntile * BN + wv * (BN / kWavesN) + pass * WPP + lc % WPP;
+                        col = ntile * BN + wv * (BN / kWN) + pass * WPP + lc % WPP;
                     }
                     if (row < rows)
                         *(u32x4_t*)&Cseg[(size_t)(row0 + m0 + row) * N + col] =
@@ -595,14 +601,24 @@ __global__ __launch_bounds__(128 * kWavesN, 1) void k_grouped_gemm(GemmParams p)
                 __syncthreads();
             }
         };
-        if (hgt > 224) run_tile(IntC<8>{});
-        else if (hgt > 192) run_tile(IntC<7>{});
-        else if (hgt > 160) run_tile(IntC<6>{});
-        else if (hgt > 128) run_tile(IntC<5>{});
-        else if (hgt > 96) run_tile(IntC<4>{});
-        else if (hgt > 64) run_tile(IntC<3>{});
-        else if (hgt > 32) run_tile(IntC<2>{});
-        else run_tile(IntC<1>{});
+        if constexpr (BM == 384) {
+            const int rt = hgt / 64;
+            if (rt >= 6) run_tile(IntC<6>{});
+            else if (rt == 5) run_tile(IntC<5>{});
+            else if (rt == 4) run_tile(IntC<4>{});
+            else if (rt == 3) run_tile(IntC<3>{});
+            else if (rt == 2) run_tile(IntC<2>{});
+            else run_tile(IntC<1>{});
+        } else {
+            if (hgt > 224) run_tile(IntC<8>{});
+            else if (hgt > 192) run_tile(IntC<7>{});
+            else if (hgt > 160) run_tile(IntC<6>{});
+            else if (hgt > 128) run_tile(IntC<5>{});
+            else if (hgt > 96) run_tile(IntC<4>{});
+            else if (hgt > 64) run_tile(IntC<3>{});
+            else if (hgt > 32) run_tile(IntC<2>{});
+            else run_tile(IntC<1>{});
+        }
     }
 }
 
@@ -674,13 +690,13 @@ __global__ __launch_bounds__(64) void k_zero_ctr(int* ctr)
     if (threadIdx.x < 16) ctr[threadIdx.x] = 0;
 }
 
-template <bool UP, int BN>
+template <bool UP, int BN, int BMT>
 hipError_t launch_gemm_t(const GemmParams& p, long long ub, hipStream_t s)
 {
     // one resident block per CU (four LDS stages: 96 or 128 KB)
     long long grid = std::min<long long>(ub, (long long)num_cus());
     grid = (grid + 7) / 8 * 8;
-    hipLaunchKernelGGL((k_grouped_gemm<UP, BN>), dim3((unsigned)grid), dim3(128 * kWavesN), 0, s, p);
+    hipLaunchKernelGGL((k_grouped_gemm<UP, BN, BMT>), dim3((unsigned)grid), dim3(512), 0, s, p);
     return hipGetLastError();
 }
 
@@ -729,15 +745,19 @@ hipError_t launch_gemm(const moe_cfg& c, const FfnArgs& a, bool up, hipStream_t 
     const int nw_r = up ? 2 * c.I : c.H;
     const int nw_s = up ? 2 * a.Ish : c.H;
     const bool wide = (a.n_routed == 0 || nw_r % 256 == 0) && (!p.has_shared || nw_s % 256 == 0);
+    // otherwise (N a multiple of 128 only) 384 x 128 tiles, waves 4 x 2: a
+    // third fewer LDS fragment bytes per output than 256 x 128 with waves
+    // 2 x 4, and a segment of up to 384 rows reads its weight tile once
     const int BN = wide ? 256 : 128;
+    const int TBM = wide ? BM : 384;
     // host upper bound on the tile count (A is only known on the device)
     long long ub = 0;
-    if (a.n_routed > 0) ub += ((long long)ceil_div(a.A_max, BM) + a.n_routed) * (nw_r / BN);
-    if (p.has_shared) ub += (long long)ceil_div(c.T, BM) * (nw_s / BN);
+    if (a.n_routed > 0) ub += ((long long)ceil_div(a.A_max, TBM) + a.n_routed) * (nw_r / BN);
+    if (p.has_shared) ub += (long long)ceil_div(c.T, TBM) * (nw_s / BN);
     if (ub == 0) return hipSuccess;
-    if (up)
-        return wide ? launch_gemm_t<true, 256>(p, ub, s) : launch_gemm_t<true, 128>(p, ub, s);
-    return wide ? launch_gemm_t<false, 256>(p, ub, s) : launch_gemm_t<false, 128>(p, ub, s);
+    if (!wide)
+        return up ? launch_gemm_t<true, 128, 384>(p, ub, s) : launch_gemm_t<false, 128, 384>(p, ub, s);
+    return up ? launch_gemm_t<true, 256, 256>(p, ub, s) : launch_gemm_t<false, 256, 256>(p, ub, s);
 }
 
 hipError_t launch_f32(const moe_cfg& c, const FfnArgs& a, bool up, hipStream_t s)
