@@ -12,7 +12,10 @@
 namespace moe {
 namespace {
 
-constexpr int kBM = 16;        // tokens per block
+// Tokens per route block: 16 (one MFMA row tile) when the kernel computes
+// the gate itself (E <= 64), 8 when it only sums the tiled gate kernel's
+// partial logits and selects (E > 64): one token per wave, twice the blocks.
+constexpr int route_tokens(int ntw) { return ntw >= 2 ? 8 : 16; }
 constexpr int kThreads = 512;  // 8 waves
 constexpr int kWaves = kThreads / 64;
 
@@ -226,6 +229,8 @@ template <int NTW, bool BF16>
 __global__ __launch_bounds__(kThreads) void k_route(RouteParams p)
 {
     constexpr int EP = NTW * 64;  // experts padded to a multiple of 64
+    constexpr int kBM = route_tokens(NTW);
+    static_assert(kBM % kWaves == 0, "whole tokens per wave");
     __shared__ float s_log[kBM][EP + 4];
     __shared__ int s_s2o[EP];
     __shared__ int s_o2s[EP];
@@ -288,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void k_route(RouteParams p)
             }
             s_log[row][col] = sum;
         }
-    } else if constexpr (BF16) {
+    } else if constexpr (BF16 && kBM == 16) {
         // MFMA 16x16x32 bf16.  Lane l feeds token row (l & 15) and expert
         // column (l & 15) of its tile; its 4-lane group kg = l >> 4 owns the
         // contiguous k-range [16kg, 16kg+16) of every 64-wide chunk, split over
@@ -549,8 +554,11 @@ __global__ __launch_bounds__(kThreads) void k_route(RouteParams p)
 template <bool BF16>
 hipError_t launch_route_t(const RouteParams& p, hipStream_t s)
 {
-    const dim3 grid(ceil_div(p.T, kBM)), block(kThreads);
+    const dim3 block(kThreads);
     const int ntw = ceil_div(p.E, 64);
+    // bf16 layers with E > 64 take their logits from the tiled gate kernel
+    if (BF16 && ntw >= 2 && p.glog == nullptr) return hipErrorInvalidValue;
+    const dim3 grid(ceil_div(p.T, route_tokens(ntw)));
     if (ntw <= 1)
         hipLaunchKernelGGL((k_route<1, BF16>), grid, block, 0, s, p);
     else if (ntw <= 2)
