@@ -281,7 +281,8 @@ int32_t moe_sag(const moe_cfg* cfg, const void* y, const int32_t* tok_perm, void
  */
 
 /* Token step counts: counts[v*P + g] = assignments of token ID v on experts
- * e with group[e] = g (counts [V*P] int32, device, overwritten). */
+ * e with group[e] = g (counts [V*P] int32, device, overwritten; V*P < 2^31,
+ * else MOE_ESHAPE). */
 int32_t moe_token_group_counts(const moe_cfg* cfg, int32_t n_tok, const int32_t* row_ptr,
                                const int32_t* expert, const int32_t* tok, const int32_t* group,
                                int32_t* counts, void* stream);

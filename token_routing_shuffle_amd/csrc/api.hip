@@ -418,6 +418,7 @@ MOE_API int32_t moe_token_group_counts(const moe_cfg* cfg, int32_t n_tok, const 
     if (rc != MOE_OK) return rc;
     const moe_cfg& c = *cfg;
     if (n_tok < 0) return fail(MOE_EINVAL, "n_tok < 0");
+    if ((long long)c.V * c.P >= (1LL << 31)) return fail(MOE_ESHAPE, "V*P must stay below 2^31 (token table)");
     REQUIRE(counts);
     if (n_tok > 0) {
         REQUIRE(row_ptr);
@@ -483,6 +484,7 @@ MOE_API int32_t moe_optimize_placement(const moe_cfg* cfg, int32_t n_tok, const 
     const moe_cfg& c = *cfg;
     const int E = c.E, P = c.P, epg = c.E / c.P;
     if (n_tok < 0 || max_iters < 1) return fail(MOE_EINVAL, "n_tok < 0 or max_iters < 1");
+    if ((long long)c.V * c.P >= (1LL << 31)) return fail(MOE_ESHAPE, "V*P must stay below 2^31 (token table)");
     REQUIRE(group);
     REQUIRE(lut);
     REQUIRE(counts_vp);

@@ -36,8 +36,12 @@ __global__ __launch_bounds__(kThreads) void k_fill_i32(int32_t* p, long long n, 
         p[i] = v;
 }
 
-// D[v][g] += 1 for every assignment (token t, expert e): v = tok[t], g = group[e]
-__global__ __launch_bounds__(kThreads) void k_token_group_counts(int n_tok, int V, int E, int P,
+// D[v][g] += 1 for every assignment (token t, expert e): v = tok[t], g = group[e].
+// Thread per token; the wave's lanes take their j-th assignments together and
+// lanes with the same (v, g) key add their count with one atomic (the lowest
+// of them): frequent token ids would otherwise serialise thousands of
+// atomics on a few counters.
+__global__ __launch_bounds__(kThreads) void k_token_group_counts(int n_tok, int V, int E, int P, int key_bits,
                                                                  const int32_t* __restrict__ row_ptr,
                                                                  const int32_t* __restrict__ expert,
                                                                  const int32_t* __restrict__ tok,
@@ -45,14 +49,29 @@ __global__ __launch_bounds__(kThreads) void k_token_group_counts(int n_tok, int 
                                                                  int32_t* __restrict__ D)
 {
     const int t = blockIdx.x * kThreads + threadIdx.x;
-    if (t >= n_tok) return;
-    const int v = tok[t];
-    if ((unsigned)v >= (unsigned)V) return;
-    for (int a = row_ptr[t]; a < row_ptr[t + 1]; ++a) {
-        const int e = expert[a];
-        if ((unsigned)e >= (unsigned)E) continue;
-        const int g = group[e];
-        if ((unsigned)g < (unsigned)P) atomicAdd(&D[(size_t)v * P + g], 1);
+    int v = t < n_tok ? tok[t] : -1;
+    const bool ok = t < n_tok && (unsigned)v < (unsigned)V;
+    const int a0 = ok ? row_ptr[t] : 0;
+    const int n = ok ? row_ptr[t + 1] - a0 : 0;
+    int nmax = n;  // wave-uniform loop bound: every lane takes part in the ballots
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) nmax = max(nmax, __shfl_xor(nmax, o));
+    for (int j = 0; j < nmax; ++j) {
+        bool valid = j < n;
+        uint32_t key = 0;
+        if (valid) {
+            const int e = expert[a0 + j];
+            valid = (unsigned)e < (unsigned)E;
+            if (valid) {
+                const int g = group[e];
+                valid = (unsigned)g < (unsigned)P;
+                key = (uint32_t)(v * P + g);
+            }
+        }
+        const uint64_t act = __ballot(valid);
+        if (act == 0) continue;
+        const uint64_t peers = match_key(key, key_bits, act);
+        if (valid && (peers & lanemask_lt()) == 0) atomicAdd(&D[key], (int)__popcll(peers));
     }
 }
 
@@ -140,7 +159,7 @@ hipError_t launch_token_group_counts(int n_tok, int V, int E, int P, const int32
     hipError_t e = launch_fill_i32(D, (long long)V * P, 0, s);
     if (e != hipSuccess || n_tok == 0) return e;
     hipLaunchKernelGGL(k_token_group_counts, dim3((unsigned)ceil_div(n_tok, kThreads)), dim3(kThreads),
-                       0, s, n_tok, V, E, P, row_ptr, expert, tok, group, D);
+                       0, s, n_tok, V, E, P, ilog2(V * P), row_ptr, expert, tok, group, D);
     return hipGetLastError();
 }
 
