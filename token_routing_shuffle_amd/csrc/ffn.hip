@@ -224,9 +224,10 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm(GemmParams p)
             kt = p.shK / BK;
         }
     };
-    // A segment of cnt rows is cut into mt = ceil(cnt / 256) m-tiles of
-    // equal height (a multiple of 32 rows): the tiles that share a weight tile
-    // then run at the same speed, so the second reader finds it in L2.
+    // A segment of cnt rows is cut into mt = ceil(cnt / BM) m-tiles of
+    // equal height (a multiple of kHq rows: 32, or 64 for the 384-row tiles):
+    // the tiles that share a weight tile then run at the same speed, so the
+    // second reader finds it in L2.
     auto mtile_h = [&](int cnt) {
         const int mt = (cnt + BM - 1) / BM;
         return ((cnt + mt - 1) / mt + kHq - 1) / kHq * kHq;
@@ -243,9 +244,10 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm(GemmParams p)
     {
         constexpr int SPT = (kMaxSeg + kThreads - 1) / kThreads;
         // Segments in class-major order: class c holds the segments whose
-        // m-tiles are 256 - 64c or 224 - 64c rows high (empty segments go
-        // last), in segment order inside a class.  Ranks inside a class come from two
-        // scans of 16-bit counters packed in pairs.
+        // m-tiles are BM - BM/4 * c high or a little less (256-row tiles:
+        // 256 - 64c or 224 - 64c; empty segments go last), in segment order
+        // inside a class.  Ranks inside a class come from two scans of 16-bit
+        // counters packed in pairs.
         int cls[SPT], pk01 = 0, pk23 = 0;
 #pragma unroll
         for (int q = 0; q < SPT; ++q) {
