@@ -9,14 +9,13 @@
 
 namespace moe {
 
-// Tokens per block of the histogram / scatter kernels of the shuffle.
-// (Measured: 64-token blocks at T = 4096 were slower overall, the larger
-// count table costing the single-block scan more than the shorter blocks
-// gained.)
+// Tokens per block of the histogram / scatter kernels of the shuffle: 256,
+// halved (down to 64) while the layer would get fewer than 128 blocks, so
+// that mid-sized layers still spread the histogram and scatter over many CUs.
+// (While the per-block counts were scanned by a single block, 64-token blocks
+// at T = 4096 were slower, the larger count table costing that scan more than
+// the shorter blocks gained; with one wave per bucket row they are faster.)
 constexpr int kShuffleMaxTPB = 256;
-// Tokens per counting-sort block: 256, halved (down to 64) while the layer
-// would get fewer than 128 blocks, so that mid-sized layers still spread the
-// histogram and scatter over many CUs.
 inline int shuffle_tpb(int T, int, int)
 {
     int tpb = kShuffleMaxTPB;
