@@ -142,3 +142,47 @@ def test_request_histograms_and_assignment():
     a_or = mo.assign_requests(H_or)
     assert best == sum(H_or[r, a_or[r]] for r in range(R))
     assert (np.bincount(a, minlength=cfg.P) == R // cfg.P).all()
+
+
+@pytest.mark.parametrize("hot_share", [0.6, 1.0])
+def test_token_counts_hot_ids_ragged_and_out_of_range(hot_share):
+    """The token-step counts under the heaviest key collisions (most or all
+    tokens one id, so whole waves share a (token, group) key), ragged budgets
+    including zero, and out-of-range token ids and experts, which the call
+    ignores: bit for bit against the oracle's counts of the valid entries."""
+    m = moe_mod()
+    cfg = wl.CONFIGS["dsv2lite"]
+    c = m.make_cfg(cfg)
+    E, P, V = cfg.E, cfg.P, cfg.V
+    rng = np.random.default_rng(31)
+    n = 3001
+    tok = rng.integers(0, V, n).astype(np.int32)
+    tok[rng.random(n) < hot_share] = 7
+    bad_tok = rng.random(n) < 0.02
+    tok[bad_tok] = np.where(rng.random(int(bad_tok.sum())) < 0.5, -5, V).astype(np.int32)
+    kt = rng.integers(0, cfg.k + 1, n)
+    rp = mo.row_ptr_of(kt).astype(np.int32)
+    # a token's experts: a fixed preferred set for the hot id, random otherwise
+    ex = np.concatenate([(np.arange(k) * 5 % E) if tok[t] == 7 else rng.permutation(E)[:k]
+                         for t, k in enumerate(kt)]).astype(np.int32)
+    bad_ex = rng.random(ex.size) < 0.05
+    ex[bad_ex] = np.where(rng.random(int(bad_ex.sum())) < 0.5, -1, E).astype(np.int32)
+    group = (rng.permutation(E) // (E // P)).astype(np.int32)
+    d = {k: hn.to_dev(v) for k, v in dict(rp=rp, ex=ex, tok=tok, group=group).items()}
+    D = torch.empty(V * P, dtype=torch.int32, device=hn.DEV)
+    print("[cosched] token counts, hot share %.1f, %d assignments" % (hot_share, int(rp[-1])), flush=True)
+    m.moe_token_group_counts(c, n, d["rp"], d["ex"], d["tok"], d["group"], D)
+    torch.cuda.synchronize()
+    # the valid entries only: tokens with an id in [0, V), experts in [0, E)
+    keep_t = (tok >= 0) & (tok < V)
+    rows, exs = [], []
+    for t in np.flatnonzero(keep_t):
+        e = ex[rp[t]:rp[t + 1]]
+        e = e[(e >= 0) & (e < E)]
+        rows.append(len(e))
+        exs.append(e)
+    rp_v = mo.row_ptr_of(np.array(rows, np.int64))
+    ex_v = np.concatenate(exs).astype(np.int32) if exs else np.zeros(0, np.int32)
+    D_or = mo.token_group_counts(rp_v, ex_v, tok[keep_t], group, V, P)
+    np.testing.assert_array_equal(hn.host(D).reshape(V, P), D_or)
+    assert D_or[7].sum() > 0
