@@ -13,10 +13,11 @@
 // counts and offsets, the P x P would-be all-to-all matrix and the token
 // permutation.
 //
-// Four kernels: per-block LDS histograms; a wave per bucket that turns its
+// Three kernels: per-block LDS histograms; a wave per bucket that turns its
 // row of per-block counts into offsets within the bucket (and the bucket's
-// total); one block that scans the bucket totals (E*P of them) into bucket
-// starts and writes the per-slot / per-group results; a scatter that ranks
+// total); a scatter whose blocks each scan the bucket totals (E*P of them)
+// into bucket starts in LDS (block 0 also writes the per-slot / per-group
+// results; an empty layer runs that scan as a kernel of its own) and rank
 // equal buckets inside a wave with ballots (stable: blocks, waves, chunks and
 // lanes all follow assignment order).  The global offset of (bucket k,
 // block b) is bucket_start[k] + (counts of k in blocks before b).
@@ -84,66 +85,75 @@ __global__ __launch_bounds__(kThreads) void k_rowscan(ShParams p)
     if (l == 0) p.o.rowtot[row] = carry;
 }
 
-__global__ __launch_bounds__(1024) void k_scan(ShParams p)
+// Bucket totals -> bucket starts in LDS (s_start[0..nbk], the last entry A)
+// and predicted-group starts (s_tstart[0..P]); any block size, NT threads.
+template <int NT>
+MOE_DEV void bucket_starts(const ShParams& p, int* smem, int* s_start, int* s_tstart)
 {
-    // the grouped GEMMs' tile counters start from zero for the layer
-    if (p.o.gemm_ctr != nullptr && threadIdx.x < 16) p.o.gemm_ctr[threadIdx.x] = 0;
-    __shared__ int smem[17];
-    __shared__ int s_start[kMaxBuckets + 1];  // first offset of each bucket, then A
-    __shared__ int s_tstart[65];              // first offset of each predicted group, then T
+    constexpr int kPer = (kMaxBuckets + NT - 1) / NT;  // buckets per thread
     const int nbk = p.nbk, P = p.P;
-    // bucket totals -> bucket starts (nbk <= 4096: four per thread)
-    int v[4], sum = 0;
+    int v[kPer], sum = 0;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int k = threadIdx.x * 4 + q;
+    for (int q = 0; q < kPer; ++q) {
+        const int k = threadIdx.x * kPer + q;
         v[q] = k < nbk ? p.o.rowtot[k] : 0;
         sum += v[q];
     }
     int A;
     int run = block_excl_scan(sum, smem, &A);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int k = threadIdx.x * 4 + q;
-        if (k < nbk) {
-            s_start[k] = run;
-            p.o.bstart[k] = run;
-        }
+    for (int q = 0; q < kPer; ++q) {
+        const int k = threadIdx.x * kPer + q;
+        if (k < nbk) s_start[k] = run;
         run += v[q];
     }
     if (threadIdx.x == 0) {
         s_start[nbk] = A;
-        p.o.bstart[nbk] = A;
         int t = 0;
         for (int g = 0; g < P; ++g) {
             s_tstart[g] = t;
-            p.o.tstart[g] = t;
             t += p.o.rowtot[nbk + g];
         }
         s_tstart[P] = t;
-        p.o.tstart[P] = t;
     }
     __syncthreads();
-    auto bstart = [&](int bk) { return s_start[bk]; };
-    const int E = p.E, epg = E / P;
-    for (int s = threadIdx.x; s <= E; s += 1024) {
-        const int off = bstart(s * P);
+}
+
+// The per-slot / per-group results, the pair matrix and the token offsets
+// from the LDS starts; zeroes the grouped GEMMs' tile counters.
+template <int NT>
+MOE_DEV void write_offsets(const ShParams& p, const int* s_start, const int* s_tstart)
+{
+    if (p.o.gemm_ctr != nullptr && threadIdx.x < 16) p.o.gemm_ctr[threadIdx.x] = 0;
+    const int E = p.E, P = p.P, epg = E / P;
+    for (int s = threadIdx.x; s <= E; s += NT) {
+        const int off = s_start[s * P];
         p.o.expert_off[s] = off;
-        if (s < E) p.o.expert_count[s] = bstart((s + 1) * P) - off;
+        if (s < E) p.o.expert_count[s] = s_start[(s + 1) * P] - off;
     }
-    for (int g = threadIdx.x; g <= P; g += 1024) {
-        const int off = bstart(g * epg * P);
+    for (int g = threadIdx.x; g <= P; g += NT) {
+        const int off = s_start[g * epg * P];
         p.o.group_off[g] = off;
-        if (g < P) p.o.group_count[g] = bstart((g + 1) * epg * P) - off;
+        if (g < P) p.o.group_count[g] = s_start[(g + 1) * epg * P] - off;
         p.o.tok_off[g] = s_tstart[g];
     }
     // pair_count[pg * P + g]: predicted group pg, expert group g
-    for (int i = threadIdx.x; i < P * P; i += 1024) {
+    for (int i = threadIdx.x; i < P * P; i += NT) {
         const int pg = i / P, g = i % P;
         int c = 0;
-        for (int s = g * epg; s < (g + 1) * epg; ++s) c += bstart(s * P + pg + 1) - bstart(s * P + pg);
+        for (int s = g * epg; s < (g + 1) * epg; ++s) c += s_start[s * P + pg + 1] - s_start[s * P + pg];
         p.o.pair_count[i] = c;
     }
+}
+
+// Empty layers only (no scatter runs): the offsets of zero assignments.
+__global__ __launch_bounds__(1024) void k_scan(ShParams p)
+{
+    __shared__ int smem[17];
+    __shared__ int s_start[kMaxBuckets + 1];
+    __shared__ int s_tstart[65];
+    bucket_starts<1024>(p, smem, s_start, s_tstart);
+    write_offsets<1024>(p, s_start, s_tstart);
 }
 
 __global__ __launch_bounds__(kThreads) void k_scatter(ShParams p)
@@ -159,6 +169,13 @@ __global__ __launch_bounds__(kThreads) void k_scatter(ShParams p)
     const int tw0 = min(t1, t0 + w * tpw), tw1 = min(t1, t0 + (w + 1) * tpw);
     const int nbk = p.nbk, P = p.P;
 
+    // bucket and predicted-group starts: every block scans the bucket totals
+    // itself (E*P of them); block 0 also writes the offset tables
+    __shared__ int s_smem[17];
+    __shared__ int s_start[kMaxBuckets + 1];
+    __shared__ int s_tstart[65];
+    bucket_starts<kThreads>(p, s_smem, s_start, s_tstart);
+    if (b == 0) write_offsets<kThreads>(p, s_start, s_tstart);
     for (int i = threadIdx.x; i < 4 * nbk; i += kThreads) base[i / nbk][i % nbk] = 0;
     for (int i = threadIdx.x; i < 4 * 64; i += kThreads) tbase[i / 64][i % 64] = 0;
     for (int i = threadIdx.x; i <= nt; i += kThreads) s_rp[i] = p.row_ptr[t0 + i];
@@ -173,7 +190,7 @@ __global__ __launch_bounds__(kThreads) void k_scatter(ShParams p)
     __syncthreads();
     // counts -> starting positions: block offset + earlier waves' counts
     for (int i = threadIdx.x; i < nbk; i += kThreads) {
-        int run = p.o.bstart[i] + p.o.hist[(size_t)i * p.nb + b];
+        int run = s_start[i] + p.o.hist[(size_t)i * p.nb + b];
         for (int q = 0; q < 4; ++q) {
             const int c = base[q][i];
             base[q][i] = run;
@@ -181,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void k_scatter(ShParams p)
         }
     }
     if (threadIdx.x < P) {
-        int run = p.o.tstart[threadIdx.x] + p.o.thist[threadIdx.x * p.nb + b];
+        int run = s_tstart[threadIdx.x] + p.o.thist[threadIdx.x * p.nb + b];
         for (int q = 0; q < 4; ++q) {
             const int c = tbase[q][threadIdx.x];
             tbase[q][threadIdx.x] = run;
@@ -307,8 +324,10 @@ hipError_t launch_shuffle(const moe_cfg& c, int nb, int tpb, const int32_t* row_
     // the histogram kernel also runs for T == 0 so the table it writes is zero
     hipLaunchKernelGGL(k_hist, dim3(nb), dim3(kThreads), 0, s, p);
     hipLaunchKernelGGL(k_rowscan, dim3(ceil_div(p.nbk + c.P, 4)), dim3(kThreads), 0, s, p);
-    hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, p);
-    if (c.T > 0) hipLaunchKernelGGL(k_scatter, dim3(nb), dim3(kThreads), 0, s, p);
+    if (c.T > 0)
+        hipLaunchKernelGGL(k_scatter, dim3(nb), dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, p);
     return hipGetLastError();
 }
 
