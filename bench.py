@@ -33,6 +33,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--fuse-gather", type=int, default=int(os.environ.get("MOE_BENCH_FUSE_GATHER", "1")))
+    ap.add_argument("--blocked-weights", type=int, default=1,
+                    help="1: expert weights packed once (untimed) into the tile-blocked layout the "
+                         "grouped GEMMs read as contiguous blocks (moe_pack_weights); 0: row-major")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the sections after the layer (SRS/SAG, one device's share, "
@@ -87,7 +90,17 @@ def main():
     del prof_x
     epg = cfg.E // cfg.P
     d["lut"] = offline.lut_of_grouping(cfg, *prof, np.arange(cfg.E, dtype=np.int32) // epg)
-    c = moe.make_cfg(cfg, fuse_gather=args.fuse_gather)
+    blocked = int(args.blocked_weights and cfg.dtype == "bf16")
+    c = moe.make_cfg(cfg, fuse_gather=args.fuse_gather, weights_blocked=blocked)
+    if blocked:
+        # one-time layout step, like the slot permutation: not part of the layer step
+        for which, k13, k2 in ((moe.MOE_FFN_ROUTED, "W13", "W2"), (moe.MOE_FFN_SHARED, "Wsh13", "Wsh2")):
+            if d.get(k13) is None:
+                continue
+            b13, b2 = torch.empty_like(d[k13]), torch.empty_like(d[k2])
+            moe.moe_pack_weights(c, which, d[k13], d[k2], b13, b2)
+            d[k13], d[k2] = b13, b2
+        torch.cuda.synchronize()
     ws = moe.workspace(c)
     T, E, P = cfg.T, cfg.E, cfg.P
     tok = torch.as_tensor(tables.tok, device=dev)
@@ -195,6 +208,7 @@ def main():
                                                                  cfg.I, P, cfg.V)
                    if args.workload == "dsv2lite" else args.workload,
                    "tokens": T, "assignments": A, "fuse_gather": args.fuse_gather,
+                   "weights_blocked": blocked,
                    "lar": round(float(np.trace(pc)) / max(A, 1), 4),
                    "max_over_mean_expert_load": round(float(counts.max() / max(counts.mean(), 1e-9)), 3)},
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},

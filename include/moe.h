@@ -107,6 +107,9 @@ typedef struct moe_cfg {
     float aff_bias;       /* logit bias on a token's preferred experts */
     int32_t fuse_gather;  /* moe_forward: 1 = GEMM1 reads x rows through the
                              permutation instead of materialising x_sorted */
+    int32_t weights_blocked; /* bf16: 1 = the W13/W2 arrays (routed and shared)
+                                passed to moe_expert_ffn / moe_forward are in the
+                                tile-blocked layout moe_pack_weights writes */
 } moe_cfg;
 
 /*
@@ -338,6 +341,22 @@ int32_t moe_request_group_hist(const moe_cfg* cfg, int32_t n_req, const int32_t*
  *   x[n], y[n]  device fp32 arrays (y may equal x); n >= 0.
  * MOE_EINVAL for n < 0 or a NULL pointer with n > 0. */
 int32_t moe_sigmoid(const float* x, float* y, int64_t n, void* stream);
+
+/* Weights in the tile-blocked layout (bf16 layers; for callers that set
+ * cfg->weights_blocked).  The grouped GEMMs read a weight tile's 64-wide
+ * k-step as one contiguous block instead of a 128-byte piece of each of its
+ * rows, which lie a whole row apart in the row-major layout: per expert,
+ * for each n-tile j and k-step kt, the block [BN rows][64 elements] at
+ * ((j * K/64 + kt) * BN) * 64 elements; for W13 a block's rows are the
+ * tile's BN/2 W1 rows followed by the matching BN/2 W3 rows, for W2 the
+ * tile's BN rows of W2.  BN = 256 when 2*I, 2*n_shared*I_shared and H are
+ * multiples of 256, else 128 (the GEMMs' own tile width).
+ *   which = MOE_FFN_ROUTED: W13 [E,2I,H], W2 [E,H,I];
+ *   which = MOE_FFN_SHARED: W13 = Wsh13 [2*ns*Is,H], W2 = Wsh2 [H,ns*Is].
+ * The outputs W13_blk, W2_blk have the inputs' sizes (device, distinct
+ * from the inputs).  A one-time step, like the slot permutation. */
+int32_t moe_pack_weights(const moe_cfg* cfg, int32_t which, const void* W13, const void* W2,
+                         void* W13_blk, void* W2_blk, void* stream);
 
 /* Device tensors of one layer for moe_forward (host struct of device pointers). */
 typedef struct moe_weights {

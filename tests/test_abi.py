@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
         "moe_route_workspace_bytes",
         "moe_token_group_counts", "moe_lut_from_counts", "moe_expert_group_counts",
         "moe_balanced_assign", "moe_optimize_placement", "moe_request_group_hist",
-        "moe_sigmoid"])
+        "moe_sigmoid", "moe_pack_weights"])
 
 
 def test_library_exports_every_declared_symbol(m):
@@ -44,8 +44,8 @@ def test_library_exports_every_declared_symbol(m):
 
 
 def test_struct_layouts_match_header(m):
-    # moe_cfg: 20 int32/float fields, no padding; moe_exports: 17 pointers
-    assert ctypes.sizeof(m.moe_cfg) == 20 * 4
+    # moe_cfg: 21 int32/float fields, no padding; moe_exports: 17 pointers
+    assert ctypes.sizeof(m.moe_cfg) == 21 * 4
     assert ctypes.sizeof(m.moe_weights) == 9 * 8
     assert ctypes.sizeof(m.moe_inputs) == 3 * 8
     assert ctypes.sizeof(m.moe_exports) == 17 * 8

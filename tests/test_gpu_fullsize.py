@@ -1,5 +1,7 @@
 """GPU parity at the full layer sizes, in the launch configuration bench.py
-times (moe_forward with the bench's gather setting).
+times (moe_forward with the bench's gather setting and, for bf16 layers, its
+tile-blocked weights).  The determinism re-run uses the row-major weights, so
+it also checks the two weight layouts against each other bit for bit.
 
 The oracle computes routing for every token (selection compared with the
 near-tie rule, CSR offsets exactly), the dispatch metadata for the whole
@@ -35,10 +37,27 @@ def _full_case(name):
     return hn.make_case(name, profile_tokens=65536)
 
 
+def _blocked_dev(c):
+    """The layer's device weights with the expert FFN weights packed into the
+    tile-blocked layout (as bench.py does once before timing)."""
+    from token_routing_shuffle_amd import moe
+    cfg = moe.make_cfg(c.cfg, weights_blocked=1)
+    dev = dict(c.dev)
+    for which, k13, k2 in ((moe.MOE_FFN_ROUTED, "W13", "W2"), (moe.MOE_FFN_SHARED, "Wsh13", "Wsh2")):
+        if dev.get(k13) is None:
+            continue
+        b13, b2 = torch.empty_like(dev[k13]), torch.empty_like(dev[k2])
+        moe.moe_pack_weights(cfg, which, dev[k13], dev[k2], b13, b2)
+        dev[k13], dev[k2] = b13, b2
+    torch.cuda.synchronize()
+    return dev
+
+
 def _check(c):
     cfg = c.cfg
     T, E, P = cfg.T, cfg.E, cfg.P
-    r = run_forward(c, fuse=BENCH_FUSE)
+    kw = dict(dev=_blocked_dev(c), weights_blocked=1) if cfg.dtype == "bf16" else {}
+    r = run_forward(c, fuse=BENCH_FUSE, **kw)
     print("[fullsize] %s: forward done" % cfg.name, flush=True)
     l64, sel_or, w_or, rp_or, slot_or, _ = oracle_routing(c)
     np.testing.assert_array_equal(r["row_ptr"][:T + 1], rp_or)
@@ -70,7 +89,8 @@ def _check(c):
     print("[fullsize] %s: T=%d A=%d near-tie tokens=%d LAR=%.3f sampled rel err=%.3g over %d tokens"
           % (cfg.name, T, A, ndiff, ref["lar"], err, len(rows)), flush=True)
     assert err <= hn.tol_out(cfg)
-    # run-to-run determinism at full size
+    # run-to-run determinism at full size (row-major weights: the same bits)
+    kw.clear()
     r2 = run_forward(c, fuse=BENCH_FUSE, exports=False)
     assert torch.equal(r["out"], r2["out"])
 

@@ -226,9 +226,9 @@ def test_combine(key):
         assert err <= bound
 
 
-def run_forward(c, fuse=0, exports=True):
+def run_forward(c, fuse=0, exports=True, dev=None, **over):
     m = moe_mod()
-    cfg = m.make_cfg(c.cfg, fuse_gather=fuse)
+    cfg = m.make_cfg(c.cfg, fuse_gather=fuse, **over)
     T, E, P, H, A_max = c.cfg.T, c.cfg.E, c.cfg.P, c.cfg.H, c.cfg.T * c.cfg.k
     ex = {}
     if exports:
@@ -240,7 +240,7 @@ def run_forward(c, fuse=0, exports=True):
     out = torch.empty((max(T, 1), H), dtype=hn.act_dtype(c.cfg), device=hn.DEV)
     ws = m.workspace(cfg)
     k_tok = None if k_tok_of(c) is None else torch.as_tensor(k_tok_of(c), device=hn.DEV)
-    m.moe_forward(cfg, m.weights_struct(c.dev),
+    m.moe_forward(cfg, m.weights_struct(c.dev if dev is None else dev),
                   m.inputs_struct(c.x, torch.as_tensor(c.tok, device=hn.DEV), k_tok), out,
                   m.exports_struct(ex) if exports else None, ws)
     torch.cuda.synchronize()
@@ -286,6 +286,29 @@ def test_forward_deterministic_and_gather_fusion(key):
     f = run_forward(c, fuse=1, exports=False)["out"]
     assert torch.equal(a, b)
     assert torch.equal(a, f)
+
+
+@pytest.mark.parametrize("key", ["dsv2lite_1000", "qwen3_1500", "prism_1000"])
+def test_blocked_weights_bit_identical(key):
+    """Weights in the tile-blocked layout (moe_pack_weights; 256-wide tiles,
+    and for the MoE-Prism shape's GEMM1 the 128-wide ones) give the layer the
+    same bits as the row-major weights: the GEMMs stage the same operand
+    bytes, only read from other addresses."""
+    c = case(key)
+    m = moe_mod()
+    a = run_forward(c, fuse=1, exports=False)["out"]
+    cfg = m.make_cfg(c.cfg, fuse_gather=1, weights_blocked=1)
+    dev = dict(c.dev)
+    for which, k13, k2 in ((m.MOE_FFN_ROUTED, "W13", "W2"), (m.MOE_FFN_SHARED, "Wsh13", "Wsh2")):
+        if dev.get(k13) is None:
+            continue
+        b13, b2 = torch.empty_like(dev[k13]), torch.empty_like(dev[k2])
+        m.moe_pack_weights(cfg, which, dev[k13], dev[k2], b13, b2)
+        dev[k13], dev[k2] = b13, b2
+    torch.cuda.synchronize()
+    print("[blocked] %s" % key, flush=True)
+    b = run_forward(c, fuse=1, exports=False, dev=dev, weights_blocked=1)["out"]
+    assert torch.equal(a, b)
 
 
 @pytest.mark.parametrize("name,T", [("dsv2lite", 600), ("tiny", 64), ("prism", 384)])

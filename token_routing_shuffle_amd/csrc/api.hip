@@ -79,6 +79,8 @@ int32_t check_cfg(const moe_cfg* cp)
             return fail(MOE_EINVAL, "route_scale must be finite");
     }
     if (!(c.aff_bias == c.aff_bias)) return fail(MOE_EINVAL, "aff_bias is NaN");
+    if (c.weights_blocked != 0 && c.weights_blocked != 1) return fail(MOE_EINVAL, "weights_blocked must be 0 or 1");
+    if (c.weights_blocked && c.dtype != MOE_BF16) return fail(MOE_EDTYPE, "blocked weights need bf16");
     return MOE_OK;
 }
 
@@ -568,6 +570,29 @@ MOE_API int32_t moe_request_group_hist(const moe_cfg* cfg, int32_t n_req, const 
     hipError_t e = launch_request_group_hist(n_req, cfg->V, cfg->P, req_ptr, tok, lut, hist,
                                              (hipStream_t)stream);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_request_group_hist");
+}
+
+MOE_API int32_t moe_pack_weights(const moe_cfg* cfg, int32_t which, const void* W13, const void* W2,
+                                 void* W13_blk, void* W2_blk, void* stream)
+{
+    int32_t rc = check_cfg(cfg);
+    if (rc != MOE_OK) return rc;
+    const moe_cfg& c = *cfg;
+    if (c.dtype != MOE_BF16) return fail(MOE_EDTYPE, "blocked weights need bf16");
+    if (which != MOE_FFN_ROUTED && which != MOE_FFN_SHARED) return fail(MOE_EINVAL, "which must be ROUTED or SHARED");
+    const bool shared = which == MOE_FFN_SHARED;
+    if (shared && c.n_shared == 0) return fail(MOE_EINVAL, "no shared experts");
+    REQUIRE(W13);
+    REQUIRE(W2);
+    REQUIRE(W13_blk);
+    REQUIRE(W2_blk);
+    REQUIRE16(W13);
+    REQUIRE16(W2);
+    REQUIRE16(W13_blk);
+    REQUIRE16(W2_blk);
+    if (W13 == W13_blk || W2 == W2_blk) return fail(MOE_EINVAL, "blocked weights must not alias their source");
+    hipError_t e = launch_pack_weights(c, shared, W13, W2, W13_blk, W2_blk, (hipStream_t)stream);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_pack_weights");
 }
 
 MOE_API int32_t moe_sigmoid(const float* x, float* y, int64_t n, void* stream)

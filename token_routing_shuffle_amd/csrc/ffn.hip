@@ -68,6 +68,7 @@ struct GemmParams {
     uint16_t* shC;           // up: h_sh [T, Ish]; down: y_sh [T, H]
     int shK, shN;
     int A_max;               // rows of the sorted row space (bounds of A, C)
+    int blocked;             // B in the tile-blocked layout (moe_pack_weights)
     int* ctr;                // [8] tile counters, one per XCD, zero at launch
 };
 
@@ -462,11 +463,13 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm(GemmParams p)
                     } else {
                         brow = ntile * BN + r;
                     }
-                    doff[jj] = brow * K * 2 + chunk * 16;
+                    // blocked: row r of the n-tile's contiguous [BN][64] block
+                    doff[jj] = p.blocked ? (ntile * KT * BN + r) * 128 + chunk * 16 : brow * K * 2 + chunk * 16;
                 }
             }
             auto dma = [&](int kt, int st) {
                 const int ko = kt * BK * 2;
+                const int kob = p.blocked ? kt * BN * 128 : ko;  // B: next block, or next 128 bytes of each row
 #pragma unroll
                 for (int jj = 0; jj < NI; ++jj) {
                     const int q = w * NI + jj;
@@ -475,10 +478,11 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm(GemmParams p)
                     if (q < NA)
                         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, MOE_LDS_PTR(dst), 16, doff[jj], ko, 0, 0);
                     else
-                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, MOE_LDS_PTR(dst), 16, doff[jj], ko, 0, 0);
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, MOE_LDS_PTR(dst), 16, doff[jj], kob, 0, 0);
 #else
                     (void)dst;
                     (void)ko;
+                    (void)kob;
 #endif
                 }
             };
@@ -702,6 +706,46 @@ hipError_t launch_gemm_t(const GemmParams& p, long long ub, hipStream_t s)
     return hipGetLastError();
 }
 
+// 256-wide tiles when every segment's N of this layer splits into them (the
+// rule for blocked weights, whose layout is fixed per layer).
+bool gemm_wide(const moe_cfg& c, bool up)
+{
+    const long long Ish = (long long)c.n_shared * c.I_shared;
+    const long long nw_r = up ? 2LL * c.I : c.H, nw_s = up ? 2 * Ish : c.H;
+    return nw_r % 256 == 0 && (Ish == 0 || nw_s % 256 == 0);
+}
+
+// dst = src (one operand of nexp experts, rows x K) in the tile-blocked
+// layout: chunk d of 8 elements is chunk c8 of row r of block (e, j, kt).
+__global__ __launch_bounds__(256) void k_pack(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
+                                              long long nchunks, int rows, int half_rows, int K, int BN, int up)
+{
+    const int KT = K / 64, nt = rows / BN, npt = BN / 2;
+    for (long long d = (long long)blockIdx.x * 256 + threadIdx.x; d < nchunks; d += (long long)gridDim.x * 256) {
+        const int c8 = (int)(d & 7);
+        long long rem = d >> 3;
+        const int r = (int)(rem % BN);
+        rem /= BN;
+        const int kt = (int)(rem % KT);
+        rem /= KT;
+        const int j = (int)(rem % nt);
+        const long long e = rem / nt;
+        const int srow = up ? (r < npt ? j * npt + r : half_rows + j * npt + (r - npt)) : j * BN + r;
+        ((u32x4_t*)dst)[d] = *(const u32x4_t*)(src + ((size_t)e * rows + srow) * K + kt * 64 + c8 * 8);
+    }
+}
+
+hipError_t launch_pack_one(const uint16_t* src, uint16_t* dst, long long nexp, int rows, int half_rows, int K,
+                           int BN, bool up, hipStream_t s)
+{
+    const long long n = nexp * rows * (long long)(K / 8);
+    if (n == 0) return hipSuccess;
+    const long long blocks = std::min<long long>((n + 255) / 256, 8192);
+    hipLaunchKernelGGL(k_pack, dim3((unsigned)blocks), dim3(256), 0, s, src, dst, n, rows, half_rows, K, BN,
+                       up ? 1 : 0);
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm(const moe_cfg& c, const FfnArgs& a, bool up, hipStream_t s)
 {
     GemmParams p;
@@ -712,6 +756,7 @@ hipError_t launch_gemm(const moe_cfg& c, const FfnArgs& a, bool up, hipStream_t 
     p.A_max = a.A_max;
     p.expert_off = a.expert_off;
     p.ctr = a.ctr + (up ? 0 : 8);
+    p.blocked = c.weights_blocked;
     // both GEMMs' counters are zeroed once, before the up projection
     if (up && !a.ctr_zeroed) hipLaunchKernelGGL(k_zero_ctr, dim3(1), dim3(64), 0, s, a.ctr);
     if (up) {
@@ -746,7 +791,8 @@ hipError_t launch_gemm(const moe_cfg& c, const FfnArgs& a, bool up, hipStream_t 
     // wide tiles (BN = 256) when every segment's N splits into them
     const int nw_r = up ? 2 * c.I : c.H;
     const int nw_s = up ? 2 * a.Ish : c.H;
-    const bool wide = (a.n_routed == 0 || nw_r % 256 == 0) && (!p.has_shared || nw_s % 256 == 0);
+    const bool wide = c.weights_blocked ? gemm_wide(c, up)
+                                        : (a.n_routed == 0 || nw_r % 256 == 0) && (!p.has_shared || nw_s % 256 == 0);
     // otherwise (N a multiple of 128 only) 384 x 128 tiles, waves 4 x 2: a
     // third fewer LDS fragment bytes per output than 256 x 128 with waves
     // 2 x 4, and a segment of up to 384 rows reads its weight tile once
@@ -815,6 +861,17 @@ hipError_t launch_ffn_up(const moe_cfg& c, const FfnArgs& a, hipStream_t s)
 hipError_t launch_ffn_down(const moe_cfg& c, const FfnArgs& a, hipStream_t s)
 {
     return c.dtype == MOE_BF16 ? launch_gemm(c, a, false, s) : launch_f32(c, a, false, s);
+}
+
+hipError_t launch_pack_weights(const moe_cfg& c, bool shared, const void* W13, const void* W2, void* W13b,
+                               void* W2b, hipStream_t s)
+{
+    const int nexp = shared ? 1 : c.E;
+    const int N = shared ? c.n_shared * c.I_shared : c.I;  // intermediate width
+    const int BNu = gemm_wide(c, true) ? 256 : 128, BNd = gemm_wide(c, false) ? 256 : 128;
+    hipError_t e = launch_pack_one((const uint16_t*)W13, (uint16_t*)W13b, nexp, 2 * N, N, c.H, BNu, true, s);
+    if (e == hipSuccess) e = launch_pack_one((const uint16_t*)W2, (uint16_t*)W2b, nexp, c.H, 0, N, BNd, false, s);
+    return e;
 }
 
 }  // namespace moe

@@ -98,6 +98,8 @@ struct FfnArgs {
 };
 hipError_t launch_ffn_up(const moe_cfg& c, const FfnArgs& a, hipStream_t s);
 hipError_t launch_ffn_down(const moe_cfg& c, const FfnArgs& a, hipStream_t s);
+hipError_t launch_pack_weights(const moe_cfg& c, bool shared, const void* W13, const void* W2, void* W13b,
+                               void* W2b, hipStream_t s);
 
 hipError_t launch_combine(const moe_cfg& c, const void* y_sorted, const int32_t* a2s,
                           const int32_t* row_ptr, const float* topk_w, const void* y_sh,

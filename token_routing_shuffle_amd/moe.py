@@ -37,7 +37,8 @@ class moe_cfg(ctypes.Structure):
         ("route_scale", ctypes.c_float),
         ("n_rgroups", ctypes.c_int32), ("topk_rgroups", ctypes.c_int32),
         ("rgroup_topn", ctypes.c_int32), ("aff_bias", ctypes.c_float),
-        ("fuse_gather", ctypes.c_int32)]
+        ("fuse_gather", ctypes.c_int32),
+        ("weights_blocked", ctypes.c_int32)]
 
 
 _vp = ctypes.c_void_p
@@ -110,6 +111,8 @@ def _load():
                                 vp, sz, vp]
     lib.moe_sigmoid.restype = i32
     lib.moe_sigmoid.argtypes = [vp, vp, ctypes.c_int64, vp]
+    lib.moe_pack_weights.restype = i32
+    lib.moe_pack_weights.argtypes = [P(moe_cfg), i32, vp, vp, vp, vp, vp]
     return lib
 
 
@@ -128,7 +131,7 @@ EXPORTED = ("moe_validate", "moe_workspace_bytes", "moe_route_workspace_bytes", 
             "moe_expert_ffn", "moe_combine", "moe_forward", "moe_srs", "moe_sag",
             "moe_token_group_counts", "moe_lut_from_counts", "moe_expert_group_counts",
             "moe_balanced_assign", "moe_optimize_placement", "moe_request_group_hist",
-            "moe_sigmoid")
+            "moe_sigmoid", "moe_pack_weights")
 
 
 def _p(t) -> Optional[int]:
@@ -165,6 +168,7 @@ def make_cfg(layer, **over) -> moe_cfg:
     c.n_rgroups, c.topk_rgroups, c.rgroup_topn = layer.n_rgroups, layer.topk_rgroups, layer.rgroup_topn
     c.aff_bias = layer.aff_bias
     c.fuse_gather = 0
+    c.weights_blocked = 0
     for k, v in over.items():
         setattr(c, k, v)
     return c
@@ -303,6 +307,13 @@ def moe_request_group_hist(cfg, n_req, req_ptr, tok, lut, hist, stream=None):
     rc = lib().moe_request_group_hist(ctypes.byref(cfg), int(n_req), _p(req_ptr), _p(tok), _p(lut),
                                       _p(hist), _stream(stream))
     _check(rc, "moe_request_group_hist")
+
+
+def moe_pack_weights(cfg, which, W13, W2, W13_blk, W2_blk, stream=None):
+    """W13/W2 (routed or shared) into the tile-blocked layout of cfg."""
+    rc = lib().moe_pack_weights(ctypes.byref(cfg), int(which), _p(W13), _p(W2), _p(W13_blk), _p(W2_blk),
+                                _stream(stream))
+    _check(rc, "moe_pack_weights")
 
 
 def moe_sigmoid(x, y, n=None, stream=None):
