@@ -123,8 +123,9 @@ typedef struct moe_cfg {
  * I % 64 == 0 and (n_shared*I_shared) % 64 == 0; sigmoid gate only with
  * n_rgroups in [1, 64] dividing E, 1 <= topk_rgroups <= n_rgroups,
  * 1 <= rgroup_topn <= min(8, E/n_rgroups), at least k_max experts in the
- * kept groups and a finite route_scale; aff_bias not NaN.  Returns MOE_OK
- * or the error code (MOE_ESHAPE, MOE_EDTYPE, MOE_EINVAL).
+ * kept groups and a finite route_scale; aff_bias not NaN; weights_blocked
+ * 0 or 1, and 1 only with bf16.  Returns MOE_OK or the error code
+ * (MOE_ESHAPE, MOE_EDTYPE, MOE_EINVAL).
  */
 int32_t moe_validate(const moe_cfg* cfg);
 
