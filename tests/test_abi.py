@@ -94,6 +94,8 @@ def test_profiling_chunks_validate(m):
     ("V", 0, "MOE_ESHAPE"),
     ("n_pref", 65, "MOE_ESHAPE"),
     ("ragged", 2, "MOE_EINVAL"),
+    ("weights_blocked", 2, "MOE_EINVAL"),
+    ("weights_blocked", -1, "MOE_EINVAL"),
     ("E", 1024, "MOE_ESHAPE"),
     ("T", 100000, "MOE_ESHAPE"),        # bf16 sorted rows 100000*6*2048*2 B > 2 GiB
 ])
@@ -145,6 +147,36 @@ def test_calls_reject_null_pointers_before_launching(m):
     assert L.moe_sigmoid(None, None, 10, None) == m.MOE_EINVAL
     assert L.moe_sigmoid(None, None, -1, None) == m.MOE_EINVAL
     assert L.moe_sigmoid(None, None, 0, None) == m.MOE_OK
+
+
+def test_blocked_weights_rules(m):
+    """The tile-blocked weight layout exists for bf16 layers only, and
+    moe_pack_weights rejects bad arguments before it launches anything."""
+    c = _cfgs(m)["dsv2lite"]
+    c.weights_blocked = 1
+    assert m.moe_validate(c) == m.MOE_OK, m.moe_last_error()
+    c.dtype = m.MOE_F32
+    assert m.moe_validate(c) == m.MOE_EDTYPE
+    c.dtype = m.MOE_BF16
+    L = m.lib()
+    ref = ctypes.byref(c)
+    fake = 1 << 40   # never dereferenced: the checks fail first
+    assert L.moe_pack_weights(ref, 5, fake, fake, fake + 4096, fake + 8192, None) == m.MOE_EINVAL
+    assert L.moe_pack_weights(ref, m.MOE_FFN_ROUTED, None, fake, fake, fake, None) == m.MOE_EINVAL
+    assert L.moe_pack_weights(ref, m.MOE_FFN_ROUTED, fake, fake, fake, fake + 8192, None) == m.MOE_EINVAL
+    assert "alias" in m.moe_last_error()
+    assert L.moe_pack_weights(ref, m.MOE_FFN_ROUTED, fake + 2, fake, fake + 4096, fake + 8192,
+                              None) == m.MOE_EINVAL
+    assert "aligned" in m.moe_last_error()
+    c.n_shared = 0
+    assert L.moe_pack_weights(ref, m.MOE_FFN_SHARED, fake, fake, fake + 4096, fake + 8192,
+                              None) == m.MOE_EINVAL
+    assert "shared" in m.moe_last_error()
+    c.n_shared = 2
+    c.dtype = m.MOE_F32
+    c.weights_blocked = 0
+    assert L.moe_pack_weights(ref, m.MOE_FFN_ROUTED, fake, fake, fake + 4096, fake + 8192,
+                              None) == m.MOE_EDTYPE
 
 
 def test_calls_reject_small_or_misaligned_workspace(m):
