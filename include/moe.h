@@ -116,9 +116,11 @@ typedef struct moe_cfg {
  * Host only; needs no GPU.  Checks the description: T >= 0 (an empty layer
  * is valid: the calls then enqueue nothing that reads a row); positive H, E,
  * P, I, V; k_max in [1, min(E, 64)]; T * k_max < 2^31 and T * k_max * H
- * < 2^40; for bf16 also T * k_max * max(H, I) * 2 and
- * T * max(H, n_shared*I_shared) * 2 below 2^31 bytes (32-bit row offsets in
- * the grouped GEMMs); E <= 512; E % P == 0 and E/P a power of two; P <= 64 and
+ * < 2^40; for bf16 (32-bit buffer offsets) also x [T,H], the gate [E,H] and
+ * one expert's [2I,H] (and the stacked shared experts' [2*n_shared*I_shared,
+ * H]) below 2^31 bytes each -- the sorted-row operands of the grouped GEMMs
+ * ([T*k_max, H] and [T*k_max, I]) are addressed per tile and have no such
+ * limit; E <= 512; E % P == 0 and E/P a power of two; P <= 64 and
  * E*P <= 4096; n_pref in [0, E]; H % 8 == 0; for bf16 H % 128 == 0,
  * I % 64 == 0 and (n_shared*I_shared) % 64 == 0; sigmoid gate only with
  * n_rgroups in [1, 64] dividing E, 1 <= topk_rgroups <= n_rgroups,
@@ -142,6 +144,13 @@ const char* moe_last_error(void);
 
 /*
  * Route: gate GEMM (MFMA), affinity bias, top-k selection and weights.
+ * Passages: each token activates the few experts its gate picks, which is
+ * what makes its row travel under expert parallelism (Semantic Parallelism,
+ * ko/de technical summary §1); the gate's columns are shuffled to place the
+ * experts, so the chosen column index is already the placement slot and the
+ * model's function is unchanged (ja technical overview §2.2A) -- the
+ * selection therefore breaks ties by ORIGINAL id; top-k as a per-request
+ * knob (MoE-Prism technical summary §1, §5) gives the ragged k_tok.
  *   x[T,H]          activations
  *   Wg[E,H]         gate rows in slot order (the shuffled gate columns)
  *   ebias[E]        fp32 per-expert selection bias in slot order, or NULL
@@ -164,7 +173,7 @@ const char* moe_last_error(void);
  *                   p); sigmoid: route_scale * s_j / sum_j s_j, s = sigmoid(l)
  *   logits[T,E]     optional fp32 export of the biased logits, slot order
  * Workspace: moe_route_workspace_bytes(cfg) bytes (device, 256-byte
- * aligned), or NULL when that is 0.  bf16 layers with E >= 128 run the gate
+ * aligned), or NULL when that is 0.  bf16 layers with E > 64 run the gate
  * GEMM as its own tiled kernel and keep its fp32 partial logits there; every
  * other layer computes the gate inside the route kernel.  MOE_EWORKSPACE if
  * it is missing or too small.
@@ -177,6 +186,12 @@ int32_t moe_route(const moe_cfg* cfg, const void* x, const void* Wg, const float
 /*
  * Shuffle: token->group lookup and the dispatch metadata (Sem-MoE's token
  * shuffle by predicted device, done on one GPU as a stable counting sort).
+ * Passages: before the MoE layer tokens are shuffled to the device that
+ * holds their predicted experts (Semantic Parallelism, de technical summary
+ * §2B, ja technical overview §2.2B), the prediction coming from a
+ * lightweight token->group table (ja technical overview §2.3); the local
+ * activation rate is the share of work that stays on its device (de §4):
+ * here trace(pair_count) / A.
  *   row_ptr, topk_slot  as produced by moe_route
  *   tok[T], lut[V]      lut[v] in [0, P): predicted placement group of token ID v
  *   x[T,H]              activations (read only if x_sorted != NULL)
@@ -202,7 +217,14 @@ int32_t moe_shuffle(const moe_cfg* cfg, const int32_t* row_ptr, const int32_t* t
                     void* ws, size_t ws_bytes, void* stream);
 
 /*
- * Expert FFN (grouped SwiGLU GEMMs on MFMA): for each row r of an expert e,
+ * Expert FFN (grouped SwiGLU GEMMs on MFMA).  Passages: each device runs the
+ * experts placed on it over the rows shuffled to it (Semantic Parallelism,
+ * ja technical overview §2.2A-B) -- one placement group's slot range is one
+ * device's share; MoE-Prism's sub-experts are neuron slices of a monolithic
+ * expert (MoE-Prism technical summary §2A), which is why each slot is a
+ * plain SwiGLU over its own rows.  The SwiGLU form itself is the evaluated
+ * models' (the pages name DeepSeek-V2-Lite and Qwen3-30B-A3B).  For each row
+ * r of an expert e,
  *   y[r] = W2_e (silu(W1_e x_r) * (W3_e x_r)), fp32 accumulation; with bf16
  *   the intermediate is rounded to bf16 before the down projection.
  * which == MOE_FFN_ROUTED:
@@ -226,7 +248,10 @@ int32_t moe_expert_ffn(const moe_cfg* cfg, int32_t which, const void* x_sorted, 
                        void* stream);
 
 /*
- * Combine (restore token order): out[t] = sum_{j<k_t} topk_w[a] *
+ * Combine (restore token order).  Passage: after the experts, the results
+ * are gathered back and put into the original token order (Semantic
+ * Parallelism, de technical summary §2B, ja technical overview §2.2B).
+ * out[t] = sum_{j<k_t} topk_w[a] *
  * y_sorted[assign_to_sorted[a]] + y_sh[t], a = row_ptr[t] + j, summed in fp32
  * in j order then rounded to the dtype.  Deterministic, no atomics.
  *   y_sh[T,H] shared-expert output or NULL.
@@ -337,8 +362,11 @@ int32_t moe_request_group_hist(const moe_cfg* cfg, int32_t n_req, const int32_t*
  * scaling; 0 below -87, +inf above 88), each step one IEEE-rounded fp32
  * operation, so any other implementation of the same steps reproduces it bit
  * for bit.  The selection of the sigmoid gate compares these values, which is
- * why they are exported for checking (DeepSeek-V3-style gating is what the
- * Sem-MoE pages evaluate on; they do not describe the gate itself).
+ * why they are exported for checking.  (The pages do not describe this gate:
+ * they name DeepSeek-V3 only as an example of a large MoE model in their
+ * problem statements, de technical summary §1 and ja §1, and evaluate on
+ * DeepSeek-V2-Lite and Qwen3-30B-A3B; the sigmoid gate with per-expert bias
+ * and group-limited selection is the DeepSeek-V3-shaped layer's own form.)
  *   x[n], y[n]  device fp32 arrays (y may equal x); n >= 0.
  * MOE_EINVAL for n < 0 or a NULL pointer with n > 0. */
 int32_t moe_sigmoid(const float* x, float* y, int64_t n, void* stream);
@@ -405,6 +433,12 @@ typedef struct moe_exports {
 /*
  * The whole layer: route -> shuffle -> gather -> expert FFN (routed and
  * shared) -> combine, enqueued on one stream.  out[T,H] in token order.
+ * Passages: the Sem-MoE layer step on one device -- routing through the
+ * shuffled gate (Semantic Parallelism, ja technical overview §2.2A), token
+ * shuffle by predicted group (de technical summary §2B, ja §2.2B-§2.3),
+ * the experts, and the restore to the original order (de §2B, ja §2.2B);
+ * the all-to-all that expert parallelism would need (ko/de §1) is replaced
+ * by the counting sort and a gather fused into the first GEMM's row loads.
  * ex may be NULL.  Workspace: moe_workspace_bytes(cfg).
  */
 int32_t moe_forward(const moe_cfg* cfg, const moe_weights* w, const moe_inputs* in, void* out,

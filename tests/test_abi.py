@@ -68,17 +68,14 @@ def test_every_workload_config_validates(m):
 
 def test_profiling_chunks_validate(m):
     """The offline profile routes its 65536-token draw in chunks; every
-    chunk's layer configuration must pass validation (k = 32 layers allow
-    at most 16383 tokens per call), and one more token must not."""
+    chunk's layer configuration must pass validation."""
     from token_routing_shuffle_amd import offline
     from token_routing_shuffle_amd import workload as wl
     for name, cfg in wl.CONFIGS.items():
         n = offline.route_chunk(cfg)
         assert 1 <= n <= 16384
         assert m.moe_validate(m.make_cfg(cfg, T=n)) == m.MOE_OK, (name, n, m.moe_last_error())
-        if n < 16384:
-            assert m.moe_validate(m.make_cfg(cfg, T=n + 1)) == m.MOE_ESHAPE, name
-    assert offline.route_chunk(wl.CONFIGS["prism"]) == 16383
+    assert offline.route_chunk(wl.CONFIGS["dsv3_prefill"].replace(H=131072)) == 8191
 
 
 @pytest.mark.parametrize("field,value,code", [
@@ -97,7 +94,7 @@ def test_profiling_chunks_validate(m):
     ("weights_blocked", 2, "MOE_EINVAL"),
     ("weights_blocked", -1, "MOE_EINVAL"),
     ("E", 1024, "MOE_ESHAPE"),
-    ("T", 100000, "MOE_ESHAPE"),        # bf16 sorted rows 100000*6*2048*2 B > 2 GiB
+    ("T", 524288, "MOE_ESHAPE"),        # bf16 x [T,H] = 524288*2048*2 B = 2 GiB
 ])
 def test_validate_rejects(m, field, value, code):
     c = _cfgs(m)["dsv2lite"]
@@ -108,11 +105,32 @@ def test_validate_rejects(m, field, value, code):
 
 
 def test_validate_accepts_rows_just_below_the_offset_limit(m):
+    """The sorted-row operands of the grouped GEMMs are addressed per tile:
+    T * k * H * 2 may exceed 2 GiB; the activations x [T,H] may not."""
     c = _cfgs(m)["dsv2lite"]
-    c.T = (2 ** 31 - 1) // (c.k_max * c.H * 2)     # 87381 tokens
+    c.T = (2 ** 31 - 1) // (c.H * 2)               # 524287 tokens, 6.4 GB of sorted rows
+    assert c.T * c.k_max * c.H * 2 > 2 ** 32
     assert m.moe_validate(c) == m.MOE_OK, m.moe_last_error()
     c.T += 1
     assert m.moe_validate(c) == m.MOE_ESHAPE
+
+
+def test_validate_rejects_weights_beyond_the_offset_limit(m):
+    """One expert's W13 [2I,H] (and the stacked shared experts', and the gate
+    [E,H]) are addressed through 32-bit buffer offsets: each must stay below
+    2 GiB."""
+    c = _cfgs(m)["dsv2lite"]
+    c.H, c.I, c.n_shared, c.I_shared = 32768, 16384 - 64, 0, 0
+    assert m.moe_validate(c) == m.MOE_OK, m.moe_last_error()   # 2*I*H*2 just below 2 GiB
+    c.I = 16384
+    assert m.moe_validate(c) == m.MOE_ESHAPE                     # exactly 2 GiB
+    c = _cfgs(m)["dsv2lite"]
+    c.H, c.n_shared, c.I_shared = 32768, 1, 16384
+    assert m.moe_validate(c) == m.MOE_ESHAPE                     # shared [2*Is,H] = 2 GiB
+    c = _cfgs(m)["dsv2lite"]
+    c.E, c.H, c.P, c.n_shared, c.I_shared = 512, 2 ** 21, 8, 0, 0
+    c.I, c.T = 64, 16
+    assert m.moe_validate(c) == m.MOE_ESHAPE                     # gate [E,H] = 2 GiB
 
 
 def test_validate_sigmoid_group_rules(m):

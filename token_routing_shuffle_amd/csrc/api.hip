@@ -59,11 +59,15 @@ int32_t check_cfg(const moe_cfg* cp)
     if ((long long)c.T * c.k_max >= (1LL << 31) || (long long)c.T * c.k_max * c.H >= (1LL << 40))
         return fail(MOE_ESHAPE, "T*k_max too large");
     if (c.dtype == MOE_BF16) {
-        // the grouped GEMMs address their row operands through 32-bit buffer offsets
-        const long long k_routed = std::max(c.H, c.I);
-        const long long k_shared = std::max<long long>(c.H, (long long)c.n_shared * c.I_shared);
-        if ((long long)c.T * c.k_max * k_routed * 2 >= (1LL << 31) || (long long)c.T * k_shared * 2 >= (1LL << 31))
-            return fail(MOE_ESHAPE, "bf16 GEMM row operands must stay below 2 GiB");
+        // 32-bit buffer offsets: the activations x [T,H] (rows gathered by the
+        // grouped GEMM and read by the gate kernel), the gate [E,H] and one
+        // expert's (or the stacked shared experts') weight matrices must each
+        // stay below 2 GiB.  Sorted-row operands are addressed per tile.
+        const long long Ish = (long long)c.n_shared * c.I_shared;
+        if ((long long)c.T * c.H * 2 >= (1LL << 31)) return fail(MOE_ESHAPE, "bf16 x [T,H] must stay below 2 GiB");
+        if ((long long)c.E * c.H * 2 >= (1LL << 31)) return fail(MOE_ESHAPE, "bf16 gate [E,H] must stay below 2 GiB");
+        if (2LL * c.I * c.H * 2 >= (1LL << 31) || 2LL * Ish * c.H * 2 >= (1LL << 31))
+            return fail(MOE_ESHAPE, "bf16 per-expert weights [2I,H] must stay below 2 GiB");
     }
     if (c.gate == MOE_GATE_SIGMOID_GROUPED) {
         if (c.n_rgroups < 1 || c.n_rgroups > 64 || c.E % c.n_rgroups != 0)

@@ -211,3 +211,76 @@ MOE_DEV uint32_t ordered_key(float f)
     const uint32_t u = __float_as_uint(g);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+
+// ---------------------------------------------------------------------------
+// LDS staging helpers of the MFMA kernels (operands DMA'd HBM/L2 -> LDS with
+// buffer_load ... lds, fragments read back with ds_read_b128).
+
+#define MOE_LDS_PTR(p) ((void __attribute__((address_space(3)))*)(p))
+
+// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left alone)
+template <int N>
+MOE_DEV void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <int V>
+struct IntC {
+    static constexpr int value = V;
+};
+
+// LDS fragment read issued as inline asm: the compiler's wait-count pass then
+// does not treat it as a read of the in-flight LDS DMA (it would drain all
+// outstanding loads before it); completion is waited for explicitly with
+// frag_wait, whose operands tie the fragments so no use moves above it.  The
+// fragment's position inside the stage is the instruction's immediate byte
+// offset, so one address register serves all fragments of an operand.
+// (The asm exists only in the device pass; the host pass never runs these.)
+template <int OFF>
+MOE_DEV bf16x8_t lds_read_b128(uint32_t addr)
+{
+    static_assert(OFF >= 0 && OFF < 65536, "ds_read offset range");
+    bf16x8_t v;
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+#else
+    (void)addr;
+    v = bf16x8_t{};
+#endif
+    return v;
+}
+
+MOE_DEV uint32_t lds_addr(const void* p)
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
+#else
+    return (uint32_t)(uintptr_t)p;
+#endif
+}
+
+template <int I, int N, typename F>
+MOE_DEV void static_for(F&& f)
+{
+    if constexpr (I < N) {
+        f(IntC<I>{});
+        static_for<I + 1, N>(f);
+    }
+}
+
+template <int NA, int NB>
+MOE_DEV void frag_wait(bf16x8_t (&a)[NA], bf16x8_t (&b)[NB])
+{
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < NA; ++i) asm volatile("" : "+v"(a[i]));
+#pragma unroll
+    for (int i = 0; i < NB; ++i) asm volatile("" : "+v"(b[i]));
+#else
+    (void)a;
+    (void)b;
+#endif
+}

@@ -41,6 +41,8 @@
 //   MFMAs of half 1
 // so a DMA has about one and a half k-steps to land and up to two stages
 // (128 KB per CU) are in flight.
+#include <atomic>
+
 #include "common.h"
 #include "internal.h"
 
@@ -91,16 +93,6 @@ MOE_DEV uint32_t pack2_bf16(float lo, float hi)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
 
-#define MOE_LDS_PTR(p) ((void __attribute__((address_space(3)))*)(p))
-
-// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left alone)
-template <int N>
-MOE_DEV void wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
 // Keeps two accumulator blocks in AGPRs up to this point of the program
 // order.  Without it the compiler hoists the epilogue's reads of all 256
 // accumulators into VGPRs at once and spills.
@@ -114,69 +106,10 @@ MOE_DEV void acc_fence(f32x4_t& a, f32x4_t& b)
 #endif
 }
 
-template <int V>
-struct IntC {
-    static constexpr int value = V;
-};
-
 // Position of 16-byte chunk c of LDS row r (128-byte rows, eight chunks):
 // c ^ (r & 7).  Measured on gfx950, MFMA fragment reads (16 rows at one
 // chunk, for either 32-wide k-half) are then free of bank conflicts.
 MOE_DEV int swz(int r, int c) { return c ^ (r & 7); }
-
-// LDS fragment read issued as inline asm: the compiler's wait-count pass then
-// does not treat it as a read of the in-flight LDS DMA (it would drain all
-// outstanding loads before it); completion is waited for explicitly with
-// frag_wait, whose operands tie the fragments so no use moves above it.  The
-// fragment's position inside the stage is the instruction's immediate byte
-// offset, so one address register serves all fragments of an operand.
-// (The asm exists only in the device pass; the host pass never runs these.)
-template <int OFF>
-MOE_DEV bf16x8_t lds_read_b128(uint32_t addr)
-{
-    static_assert(OFF >= 0 && OFF < 65536, "ds_read offset range");
-    bf16x8_t v;
-#if defined(__HIP_DEVICE_COMPILE__)
-    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
-#else
-    (void)addr;
-    v = bf16x8_t{};
-#endif
-    return v;
-}
-
-MOE_DEV uint32_t lds_addr(const void* p)
-{
-#if defined(__HIP_DEVICE_COMPILE__)
-    return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
-#else
-    return (uint32_t)(uintptr_t)p;
-#endif
-}
-
-template <int I, int N, typename F>
-MOE_DEV void static_for(F&& f)
-{
-    if constexpr (I < N) {
-        f(IntC<I>{});
-        static_for<I + 1, N>(f);
-    }
-}
-
-template <int NA, int NB>
-MOE_DEV void frag_wait(bf16x8_t (&a)[NA], bf16x8_t (&b)[NB])
-{
-#if defined(__HIP_DEVICE_COMPILE__)
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-    for (int i = 0; i < NA; ++i) asm volatile("" : "+v"(a[i]));
-#pragma unroll
-    for (int i = 0; i < NB; ++i) asm volatile("" : "+v"(b[i]));
-#else
-    (void)a;
-    (void)b;
-#endif
-}
 
 template <bool UP, int BN, int BMT>
 __global__ __launch_bounds__(512, 1) void k_grouped_gemm(GemmParams p)
@@ -404,23 +337,24 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm(GemmParams p)
 
         // ---- operands as buffer resources (base + bounds); per-lane 32-bit
         // row offsets; the k-step goes in the scalar offset.  Rows past the
-        // segment end repeat its last row.
+        // segment end repeat its last row.  A rows held in sorted order are
+        // addressed from the tile's first row (64-bit base), so only a tile's
+        // rows, not the whole sorted row space, must fit the 32-bit offsets;
+        // gathered rows are addressed from the start of x [T, K].
+        const bool gath = !shared && p.A == nullptr;
         const uint16_t* Abase;
-        int a_bytes;
-        if (shared) {
-            Abase = p.shA;
-            a_bytes = p.T * K * 2;
-        } else if (p.A != nullptr) {
-            Abase = p.A;
-            a_bytes = p.A_max * K * 2;
-        } else {
+        long long a_bytes;
+        if (gath) {
             Abase = p.X;
-            a_bytes = p.T * K * 2;
+            a_bytes = (long long)p.T * K * 2;
+        } else {
+            Abase = (shared ? p.shA : p.A) + (size_t)(row0 + m0) * K;
+            a_bytes = (long long)rows * K * 2;
         }
         const uint16_t* Bseg = shared ? p.shB : p.B + (size_t)(p.e_begin + seg) * (UP ? 2 * (size_t)N : (size_t)N) * K;
-        const int b_bytes = (UP ? 2 * N : N) * K * 2;
-        const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc((void*)Abase, (short)0, a_bytes, 0x00020000);
-        const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc((void*)Bseg, (short)0, b_bytes, 0x00020000);
+        const long long b_bytes = (long long)(UP ? 2 * N : N) * K * 2;
+        const __amdgpu_buffer_rsrc_t rsA = __builtin_amdgcn_make_buffer_rsrc((void*)Abase, (short)0, (int)a_bytes, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rsB = __builtin_amdgcn_make_buffer_rsrc((void*)Bseg, (short)0, (int)b_bytes, 0x00020000);
         const int KT = K / BK;
 
         // RT = 16-row blocks per wave: the tile has 32 * RT rows (RT = 1..8),
@@ -451,8 +385,8 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm(GemmParams p)
                 const int chunk = swz(rin, lane & 7);
                 if (q < NA) {
                     const int row = q * 8 + rin;
-                    const int gr = row0 + m0 + min(row, rows - 1);
-                    const int src_row = (!shared && p.A == nullptr) ? p.row_tok[gr] : gr;
+                    const int tr = min(row, rows - 1);
+                    const int src_row = gath ? p.row_tok[row0 + m0 + tr] : tr;
                     doff[jj] = src_row * K * 2 + chunk * 16;
                 } else {
                     const int r = (q - NA) * 8 + rin;
@@ -677,18 +611,21 @@ __global__ __launch_bounds__(256) void k_ffn_f32(F32Params p)
     }
 }
 
+// Compute units of the current device, queried once per device.  The cache
+// is written with relaxed atomics: concurrent first calls from several host
+// threads may all query, and they store the same value.
 int num_cus()
 {
-    static int cached[64] = {0};
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int v = 0;
+    int v = cached[dev].load(std::memory_order_relaxed);
+    if (v <= 0) {
         if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
             v = 256;
-        cached[dev] = v;
+        cached[dev].store(v, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return v;
 }
 
 __global__ __launch_bounds__(64) void k_zero_ctr(int* ctr)

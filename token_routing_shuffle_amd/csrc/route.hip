@@ -87,42 +87,6 @@ constexpr int kGRows = kGT + kGE;           // LDS rows per chunk
 constexpr int kGChunkE = kGRows * 64;       // bf16 elements per chunk buffer
 constexpr int kGNI = kGRows / 8 / 4;        // DMA instructions per wave per chunk
 
-#define MOE_LDS_PTR(p) ((void __attribute__((address_space(3)))*)(p))
-
-template <int N>
-MOE_DEV void g_wait_vmcnt()
-{
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
-
-template <int OFF>
-MOE_DEV bf16x8_t g_lds_read(uint32_t addr)
-{
-    static_assert(OFF >= 0 && OFF < 65536, "ds_read offset range");
-    bf16x8_t v;
-#if defined(__HIP_DEVICE_COMPILE__)
-    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
-#else
-    (void)addr;
-    v = bf16x8_t{};
-#endif
-    return v;
-}
-
-MOE_DEV void g_frag_wait(bf16x8_t (&a)[2], bf16x8_t (&b)[8][2])
-{
-#if defined(__HIP_DEVICE_COMPILE__)
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-    asm volatile("" : "+v"(a[0]), "+v"(a[1]));
-#pragma unroll
-    for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(b[i][0]), "+v"(b[i][1]));
-#else
-    (void)a;
-    (void)b;
-#endif
-}
-
 __global__ __launch_bounds__(256) void k_gate_logits(int T, int H, int E, int Kc, const uint16_t* x,
                                                       const uint16_t* Wg, float* __restrict__ glog)
 {
@@ -167,11 +131,7 @@ __global__ __launch_bounds__(256) void k_gate_logits(int T, int H, int E, int Kc
     // Fragments: lane (r = l & 15, kg = l >> 4) reads row r of its 16-row
     // block at chunks kg (first 32-wide half) and kg + 4 (second half).
     const int r = l & 15, kg = l >> 4;
-#if defined(__HIP_DEVICE_COMPILE__)
-    const uint32_t sbase = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)s_g);
-#else
-    const uint32_t sbase = 0;
-#endif
+    const uint32_t sbase = lds_addr(s_g);
     const uint32_t a_row = sbase + (w * 16 + r) * 128, b_row = sbase + (kGT + r) * 128;
     const uint32_t c0 = (uint32_t)((kg ^ (r & 7)) << 4), c1 = (uint32_t)(((kg + 4) ^ (r & 7)) << 4);
     f32x4_t acc[8];
@@ -182,34 +142,23 @@ __global__ __launch_bounds__(256) void k_gate_logits(int T, int H, int E, int Kc
     if (nch > 1) dma(1);
     for (int c = 0; c < nch; ++c) {
         // this wave's DMA of chunk c has landed (chunk c+1's may be in flight)
-        if (c + 1 < nch) g_wait_vmcnt<kGNI>(); else g_wait_vmcnt<0>();
+        if (c + 1 < nch) wait_vmcnt<kGNI>(); else wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();  // chunk c visible; chunk c-1's buffer free
         if (c + 2 < nch) dma(c + 2);
         const uint32_t so = (uint32_t)((c % kGNB) * kGChunkE * 2);
-        bf16x8_t a[2], b[8][2];
-        a[0] = g_lds_read<0>(a_row + so + c0);
-        a[1] = g_lds_read<0>(a_row + so + c1);
-        b[0][0] = g_lds_read<0 * 16 * 128>(b_row + so + c0);
-        b[0][1] = g_lds_read<0 * 16 * 128>(b_row + so + c1);
-        b[1][0] = g_lds_read<1 * 16 * 128>(b_row + so + c0);
-        b[1][1] = g_lds_read<1 * 16 * 128>(b_row + so + c1);
-        b[2][0] = g_lds_read<2 * 16 * 128>(b_row + so + c0);
-        b[2][1] = g_lds_read<2 * 16 * 128>(b_row + so + c1);
-        b[3][0] = g_lds_read<3 * 16 * 128>(b_row + so + c0);
-        b[3][1] = g_lds_read<3 * 16 * 128>(b_row + so + c1);
-        b[4][0] = g_lds_read<4 * 16 * 128>(b_row + so + c0);
-        b[4][1] = g_lds_read<4 * 16 * 128>(b_row + so + c1);
-        b[5][0] = g_lds_read<5 * 16 * 128>(b_row + so + c0);
-        b[5][1] = g_lds_read<5 * 16 * 128>(b_row + so + c1);
-        b[6][0] = g_lds_read<6 * 16 * 128>(b_row + so + c0);
-        b[6][1] = g_lds_read<6 * 16 * 128>(b_row + so + c1);
-        b[7][0] = g_lds_read<7 * 16 * 128>(b_row + so + c0);
-        b[7][1] = g_lds_read<7 * 16 * 128>(b_row + so + c1);
-        g_frag_wait(a, b);
+        bf16x8_t a[2], b[16];
+        a[0] = lds_read_b128<0>(a_row + so + c0);
+        a[1] = lds_read_b128<0>(a_row + so + c1);
+        static_for<0, 8>([&](auto it) {
+            constexpr int i = it.value;
+            b[2 * i] = lds_read_b128<i * 16 * 128>(b_row + so + c0);
+            b[2 * i + 1] = lds_read_b128<i * 16 * 128>(b_row + so + c1);
+        });
+        frag_wait(a, b);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b[i][0], acc[i], 0, 0, 0);
-            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], b[i][1], acc[i], 0, 0, 0);
+            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], b[2 * i], acc[i], 0, 0, 0);
+            acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], b[2 * i + 1], acc[i], 0, 0, 0);
         }
     }
     // D layout: lane l holds expert column (l & 15) of tile i, tokens 4*kg + v
@@ -598,7 +547,10 @@ hipError_t launch_row_ptr(const moe_cfg& c, const int32_t* k_tok, int32_t* row_p
     return hipGetLastError();
 }
 
-bool gate_tiled(const moe_cfg& c) { return c.dtype == MOE_BF16 && c.E >= kGE; }
+// bf16 layers with more than 64 experts: the route kernel's own MFMA gate is
+// compiled for one 64-wide expert tile per lane set only (E <= 64); the tiled
+// kernel clamps a partial 128-expert tile and writes only e < E.
+bool gate_tiled(const moe_cfg& c) { return c.dtype == MOE_BF16 && c.E > 64; }
 
 int gate_split(const moe_cfg& c)
 {

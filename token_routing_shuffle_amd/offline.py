@@ -46,13 +46,11 @@ def device_layer(cfg, tables, w: dict, lut: np.ndarray, device="cuda") -> dict:
 
 def route_chunk(cfg, chunk: int = 16384) -> int:
     """Largest token count <= chunk whose layer configuration passes
-    moe_validate's bf16 operand limit (every GEMM row operand below 2 GiB:
-    T*k*max(H, I)*2 and T*max(H, ns*Is)*2)."""
+    moe_validate's bf16 limit on the activations (x [T,H] below 2 GiB: the
+    gate kernel addresses its rows through 32-bit buffer offsets)."""
     if cfg.dtype != "bf16":
         return chunk
-    k_routed = max(cfg.H, cfg.I)
-    k_shared = max(cfg.H, cfg.n_shared * cfg.I_shared)
-    cap = min((2 ** 31 - 1) // (2 * cfg.k * k_routed), (2 ** 31 - 1) // (2 * k_shared))
+    cap = (2 ** 31 - 1) // (2 * cfg.H)
     return max(1, min(chunk, cap))
 
 
