@@ -17,3 +17,16 @@ def pytest_configure(config):
 def olib():
     import oracle
     return oracle.lib()
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Per-case parity counts (exact ties, near-tie tokens) collected by the
+    GPU tests; printed even under -q."""
+    try:
+        from tests import harness
+    except Exception:
+        return
+    if harness.REPORT:
+        terminalreporter.section("parity summary")
+        for line in harness.REPORT:
+            terminalreporter.write_line(line)

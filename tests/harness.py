@@ -60,7 +60,7 @@ class Case:
 
 
 def make_case(name_or_cfg, T: Optional[int] = None, profile_tokens: int = 4096,
-              identity_placement: bool = False, device=DEV, **over) -> Case:
+              identity_placement: bool = False, device=DEV, mutate=None, **over) -> Case:
     from token_routing_shuffle_amd import offline
     cfg = wl.CONFIGS[name_or_cfg] if isinstance(name_or_cfg, str) else name_or_cfg
     if T is not None:
@@ -73,6 +73,11 @@ def make_case(name_or_cfg, T: Optional[int] = None, profile_tokens: int = 4096,
         tables.perm = np.arange(cfg.E, dtype=np.int32)
     w = wl.make_weights(cfg, device)
     x = wl.make_x(cfg, device)
+    if mutate is not None:
+        # test-specific structure (duplicated gate rows, zero activations,
+        # zero selection bias) applied to the drawn inputs before anything
+        # is derived from them
+        mutate(cfg, tables, w, x)
     h = {k: host(v) for k, v in w.items()}
     h["x"] = host(x)
     case = Case(cfg, tables, w, x, h, None)
@@ -190,6 +195,166 @@ def check_selection(case: Case, sel_gpu_orig: np.ndarray, l64: np.ndarray, l_gpu
     assert len(diff_rows) <= max(1, max_frac * len(l64)), \
         "%d of %d tokens route differently" % (len(diff_rows), len(l64))
     return len(diff_rows)
+
+
+# ---------------------------------------------------------------- parity checks
+
+# Lines kept for the end-of-run summary (tests/conftest.py prints them even
+# under -q): per-case counts of exact ties and near-tie tokens.
+REPORT = []
+
+
+def report(line: str) -> None:
+    REPORT.append(line)
+    print(line, flush=True)
+
+
+def csr_to_sel(case: Case, rp, slot_flat, vals=None, fill=-1):
+    """CSR (slot ids) -> [T, k] original ids (and values), padded."""
+    T, k = case.cfg.T, case.cfg.k
+    rp = np.asarray(rp, np.int64)
+    cnt = np.diff(rp)
+    sel = np.full((T, k), fill, np.int64)
+    out = np.zeros((T, k)) if vals is not None else None
+    t_of_a = np.repeat(np.arange(T), cnt)
+    j_of_a = np.arange(int(rp[-1])) - np.repeat(rp[:-1], cnt)
+    s2o = np.asarray(case.tables.slot_to_orig, np.int64)
+    sel[t_of_a, j_of_a] = s2o[np.asarray(slot_flat, np.int64)[:int(rp[-1])]]
+    if vals is not None:
+        out[t_of_a, j_of_a] = np.asarray(vals)[:int(rp[-1])]
+    return sel, out
+
+
+def logits_orig(case: Case, logits_slot) -> np.ndarray:
+    """Exported GPU logits (slot order, fp32 [T*E]) in original expert order."""
+    T, E = case.cfg.T, case.cfg.E
+    l = np.asarray(logits_slot, np.float32)[:T * E].reshape(T, E)
+    out = np.empty_like(l)
+    out[:, case.tables.slot_to_orig] = l
+    return out
+
+
+def k_tok_of(case: Case):
+    return case.tables.k_tok if case.cfg.ragged else None
+
+
+def selection_keys32(case: Case, l32) -> np.ndarray:
+    """The fp32 selection keys of the oracle for fp32 logits l32 [T,E]."""
+    if case.cfg.gate == "softmax":
+        return np.asarray(l32, np.float32)
+    key, _ = mo.sigmoid_keys(np.asarray(l32, np.float32), case.tables.ebias)
+    return key
+
+
+def exact_tie_tokens(case: Case, key32, sel_orig, k_tok=None) -> int:
+    """Tokens whose selection depends on the tie-break: an unselected expert
+    has exactly the key of the last selected one, or two selected experts
+    have equal keys (then the selection order is the tie-break's)."""
+    T, E = key32.shape
+    n = 0
+    for t in range(T):
+        kt = case.cfg.k if k_tok is None else int(k_tok[t])
+        if kt == 0:
+            continue
+        s = sel_orig[t, :kt]
+        ks = key32[t, s]
+        if len(np.unique(ks)) < kt:
+            n += 1
+            continue
+        if kt < E:
+            rest = np.setdiff1d(np.arange(E), s)
+            if (key32[t, rest] == ks.min()).any():
+                n += 1
+    return n
+
+
+def strict_route_parity(case: Case, rp_gpu, slot_gpu, w_gpu, l_gpu32, label: str) -> dict:
+    """Tier (i) of the parity rule: the oracle's fp32 selection and its
+    weights, run on the GPU's own exported logits, against the GPU's routing.
+    row_ptr and every token's selected experts (original ids, in selection
+    order) must be identical; the weights agree to fp32 rounding of the same
+    logits.  Returns the oracle's routing on those logits and the tie count."""
+    cfg = case.cfg
+    T, E = cfg.T, cfg.E
+    k_tok = k_tok_of(case)
+    kt = np.full(T, cfg.k) if k_tok is None else np.asarray(k_tok)
+    np.testing.assert_array_equal(np.asarray(rp_gpu)[:T + 1], mo.row_ptr_of(kt), err_msg="row_ptr")
+    sel_ref, w_ref = mo.route(l_gpu32, cfg, k_tok, case.tables.ebias)
+    sel_gpu, w_gpu_tk = csr_to_sel(case, rp_gpu, slot_gpu, w_gpu)
+    bad = np.nonzero((sel_gpu != sel_ref).any(axis=1))[0]
+    assert len(bad) == 0, "%s: %d tokens select differently from the oracle on the GPU's logits, " \
+        "first %s: gpu %s oracle %s" % (label, len(bad), bad[:3], sel_gpu[bad[:3]], sel_ref[bad[:3]])
+    # weights: the same fp32 logits through fp32 exp / sigmoid, a sum of at
+    # most E terms and one division on the GPU; fp64 in the oracle
+    u = 2.0 ** -24
+    tol = (E + 16) * u * np.abs(w_ref) + 1e-30
+    werr = np.abs(w_gpu_tk - w_ref)
+    assert (werr <= tol).all(), "%s: weights differ by up to %.3g (tolerance %.3g)" % (
+        label, werr.max(), tol[np.unravel_index(np.argmax(werr - tol), tol.shape)])
+    ties = exact_tie_tokens(case, selection_keys32(case, l_gpu32), sel_ref, k_tok)
+    return dict(sel=sel_ref, w=w_ref, ties=ties)
+
+
+SHUFFLE_TABLES = ("expert_count", "expert_off", "group_count", "group_off", "pair_count",
+                  "tok_perm", "tok_off")
+
+
+def strict_shuffle_parity(case: Case, rp_gpu, slot_gpu, tables: dict, label: str) -> dict:
+    """Tier (i) for the dispatch metadata: the oracle's shuffle run on the
+    GPU's own routing (row_ptr, topk_slot) must reproduce every count,
+    offset and permutation bit for bit."""
+    cfg = case.cfg
+    T = cfg.T
+    A = int(np.asarray(rp_gpu)[T])
+    ref = mo.shuffle(np.asarray(rp_gpu)[:T + 1], np.asarray(slot_gpu)[:A], case.tok, case.lut,
+                     cfg.E, cfg.P)
+    for n in SHUFFLE_TABLES:
+        if n in tables:
+            want = ref[n].reshape(-1)
+            np.testing.assert_array_equal(np.asarray(tables[n])[:want.size], want,
+                                          err_msg="%s: %s" % (label, n))
+    for n in ("sorted_to_assign", "assign_to_sorted"):
+        if n in tables:
+            np.testing.assert_array_equal(np.asarray(tables[n])[:A], ref[n], err_msg="%s: %s" % (label, n))
+    return ref
+
+
+def check_forward(case: Case, r: dict, label: str, rows=None) -> dict:
+    """Every check of a moe_forward result with exports (harness.run_forward
+    in the tests): strict routing and shuffle parity on the GPU's own
+    logits and routing; the GPU's selection against the oracle's own fp64
+    logits under the near-tie rule; the layer output against the dense
+    oracle -- with the oracle's routing where the selections agree, with the
+    oracle's routing of the GPU logits where a near tie made them differ --
+    on every token or on `rows`."""
+    cfg = case.cfg
+    T, E = cfg.T, cfg.E
+    A = int(r["row_ptr"][T])
+    l_gpu32 = logits_orig(case, r["logits"])
+    st = strict_route_parity(case, r["row_ptr"], r["topk_slot"][:A], r["topk_w"][:A], l_gpu32, label)
+    sh = strict_shuffle_parity(case, r["row_ptr"], r["topk_slot"][:A], r, label)
+    k_tok = k_tok_of(case)
+    l64 = oracle_logits(case)
+    sel_or, w_or = oracle_route(case, l64, k_tok)
+    sel_gpu = st["sel"]
+    ndiff = check_selection(case, sel_gpu, l64, l_gpu32.astype(np.float64), k_tok)
+    rows = np.arange(T) if rows is None else np.asarray(rows)
+    same = (sel_gpu[rows] == sel_or[rows]).all(axis=1)
+    got = f64_of(host(r["out"]))[rows]
+    ref = np.zeros((len(rows), cfg.H))
+    for m, sel, w in ((same, sel_or, w_or), (~same, sel_gpu, st["w"])):
+        if m.any():
+            rr = rows[m]
+            ref[m] = mo.moe_output(case.h["x"][rr], sel[rr], w[rr], case.h["W13"], case.h["W2"], cfg.I,
+                                   case.h.get("Wsh13"), case.h.get("Wsh2"), cfg.n_shared, cfg.I_shared)
+    err = rel_err(got, ref) if len(rows) else 0.0
+    report("[parity] %s: T=%d A=%d selection bit-exact on the GPU logits (%d exact-tie tokens), "
+           "dispatch tables bit-exact; vs oracle logits %d near-tie tokens, max|dl|=%.3g; "
+           "output rel err %.3g over %d tokens (tol %g); LAR=%.3f"
+           % (label, T, A, st["ties"], ndiff, float(np.abs(l_gpu32 - l64).max()) if T else 0.0,
+              err, len(rows), tol_out(cfg), sh["lar"]))
+    assert err <= tol_out(cfg), "%s: output rel err %.3g" % (label, err)
+    return dict(strict=st, shuffle=sh, ndiff=ndiff, err=err, sel_or=sel_or, w_or=w_or, l64=l64)
 
 
 def rel_err(y, ref) -> float:
