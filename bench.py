@@ -1,15 +1,20 @@
 #!/usr/bin/env python3
 """Benchmark: one MoE layer forward (route -> shuffle -> expert FFN -> combine)
-on one MI355X, DeepSeek-V2-Lite-shaped layer (T=4096 tokens, H=2048, 64 routed
-experts top-6 + 2 shared, I=1408, P=8 placement groups), seeded synthetic
-inputs resident in HBM.
+on one MI355X, seeded synthetic inputs resident in HBM.
 
+The headline is the DeepSeek-V3-shaped prefill layer (T=8192 tokens, H=7168,
+256 routed experts with grouped sigmoid gating top-8 + 1 shared expert,
+I=2048, P=8 placement groups), the largest layer shape of the workload set.
 Prints one JSON line: tokens/s over the timed steps, the roofline position of
 the dominant kernel (the grouped GEMM1 + SwiGLU launch, timed with HIP events
 recorded around it on the layer's stream in every timed step; no other events
-are recorded in the timed steps) and the CPU oracle timed on a bounded sample
-of the same workload.  The per-stage breakdown ("stages_ms") comes from a
-further untimed pass with events around every stage.
+are recorded in the timed steps) against its binding roof (HBM bytes or MFMA
+flops, whichever takes longer at peak), the CPU oracle timed on a bounded
+sample of the same workload, and the other layer shapes of the workload set
+as extra keys ("other_layers": each layer's tokens/s, its stages against
+their rooflines and the dispatch call).  The per-stage breakdown
+("stages_ms") comes from a further untimed pass with events around every
+stage.
 """
 import argparse
 import json
@@ -23,10 +28,12 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_PEAK_TFLOPS = 2500.0
-WORKLOAD = "dsv2lite"
+WORKLOAD = "dsv3_prefill"
+OTHER_LAYERS = ("tiny", "dsv2lite", "qwen3", "dsv3_decode", "prism")
+CPU_SAMPLE = {"dsv3_prefill": 8, "dsv3_decode": 8}
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
@@ -39,29 +46,208 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the sections after the layer (SRS/SAG, one device's share, "
-                         "co-scheduling), e.g. for a per-kernel profile of the layer alone")
-    ap.add_argument("--cpu-sample", type=int, default=4096,
-                    help="tokens in the oracle's timed sample (capped at the layer's T)")
+                         "co-scheduling, the other layer shapes), e.g. for a per-kernel profile "
+                         "of the layer alone")
+    ap.add_argument("--no-other-layers", action="store_true",
+                    help="skip the other layer shapes of the workload set")
+    ap.add_argument("--other-steps", type=int, default=30,
+                    help="timed steps of each other layer shape (after 10 warm-ups)")
+    ap.add_argument("--cpu-sample", type=int, default=0,
+                    help="tokens in the oracle's timed sample (0: the workload's default, "
+                         "capped at the layer's T)")
     ap.add_argument("--copy-calib-mb", type=int, default=0,
                     help="after the timed steps, run one plain device copy of this many MiB "
                          "(reference point for HBM byte counters)")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
-def algorithmic(cfg, A):
-    """Algorithmic work per launch of each stage (bytes or flops)."""
+def algorithmic(cfg, A, n_touched=None):
+    """Algorithmic work per launch of each stage (bytes or flops).
+    n_touched: routed experts with at least one row (default: all E)."""
     T, H, I, E = cfg.T, cfg.H, cfg.I, cfg.E
     b = 2 if cfg.dtype == "bf16" else 4
     Ish = cfg.n_shared * cfg.I_shared
+    ne = E if n_touched is None else n_touched
     return {
         # flops of the grouped GEMM1 (+SwiGLU): routed rows and shared experts
         "ffn_up_flops": 2.0 * A * H * 2 * I + 2.0 * T * H * 2 * Ish,
         "ffn_down_flops": 2.0 * A * I * H + 2.0 * T * Ish * H,
+        # bytes of GEMM1: the touched experts' W1/W3 and the shared W1/W3
+        # once, x once, the SwiGLU output written once (routed and shared)
+        "ffn_up_bytes": (ne * 2.0 * I * H + 2.0 * Ish * H + T * H + A * I + T * Ish) * b,
+        # bytes of GEMM2: W2 (touched and shared), the SwiGLU output once,
+        # y_sorted and y_sh written once
+        "ffn_down_bytes": (ne * 1.0 * H * I + 1.0 * H * Ish + A * I + T * Ish + A * H
+                           + (T * H if Ish else 0)) * b,
         # bytes: read x once, write A rows (+ 8T + 12A index metadata)
         "dispatch_bytes": T * H * b + A * H * b + 8.0 * T + 12.0 * A,
         # bytes: read A rows + weights/indices, write T rows (+ shared rows)
         "combine_bytes": A * H * b + 8.0 * A + T * H * b + (T * H * b if Ish else 0),
     }
+
+
+def binding_roofline(flops, nbytes, ms):
+    """A kernel against its binding roof: whichever of HBM bytes at 8 TB/s
+    and dense bf16 MFMA flops at 2.5 PFLOP/s takes longer bounds it."""
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    t_mfma = flops / (BF16_MFMA_PEAK_TFLOPS * 1e12)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    tf = flops / (ms * 1e-3) / 1e12
+    r = {"hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "mfma_frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+         "flops_per_launch": flops, "bytes_per_launch": nbytes, "avg_launch_ms": round(ms, 4),
+         "roof_ms": round(max(t_hbm, t_mfma) * 1e3, 4)}
+    if t_hbm >= t_mfma:
+        r.update(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                 frac=round(gbs / HBM_PEAK_GBS, 4))
+    else:
+        r.update(bound="mfma", achieved=round(tf, 2), peak=BF16_MFMA_PEAK_TFLOPS, unit="TFLOP/s",
+                 frac=round(tf / BF16_MFMA_PEAK_TFLOPS, 4))
+    return r
+
+
+def describe(cfg):
+    """The layer named by what it is, with its sizes."""
+    names = {"tiny": "tiny fp32 MoE layer", "dsv2lite": "DeepSeek-V2-Lite-shaped MoE layer",
+             "qwen3": "Qwen3-30B-A3B-shaped MoE layer (prefill)",
+             "dsv3_decode": "DeepSeek-V3-shaped MoE layer (decode batch)",
+             "dsv3_prefill": "DeepSeek-V3-shaped MoE layer (prefill)",
+             "prism": "MoE-Prism sub-expert layer (Qwen3-shaped parents split 4 ways)"}
+    if cfg.gate == "softmax":
+        gate = "softmax%s" % (" renormalised" if cfg.renorm else "")
+    else:
+        gate = "sigmoid + expert bias, %d routing groups keep %d by top-%d sum, x%g" % (
+            cfg.n_rgroups, cfg.topk_rgroups, cfg.rgroup_topn, cfg.route_scale)
+    k = "ragged top-k in %s per %d-token request" % (list(cfg.k_choices), cfg.req_tokens) \
+        if cfg.ragged else "top-%d" % cfg.k
+    sh = " + %d shared (I=%d)" % (cfg.n_shared, cfg.I_shared) if cfg.n_shared else ""
+    return "%s: T=%d H=%d E=%d %s %s%s, I=%d, P=%d, V=%d, %s" % (
+        names.get(cfg.name, cfg.name), cfg.T, cfg.H, cfg.E, k, gate, sh, cfg.I, cfg.P, cfg.V, cfg.dtype)
+
+
+class Layer:
+    """One layer's device state: slot-ordered weights (optionally packed into
+    the tile-blocked layout), the token->group table from a 65536-token
+    profiling draw routed by the library, inputs, outputs and workspace."""
+
+    def __init__(self, cfg, args, fuse_gather, blocked_weights):
+        import numpy as np
+        import torch
+        from token_routing_shuffle_amd import moe, offline
+        from token_routing_shuffle_amd import workload as wl
+        dev = "cuda"
+        self.cfg = cfg
+        self.tables = tables = wl.make_tables(cfg)
+        self.w = w = wl.make_weights(cfg, dev)
+        self.x = wl.make_x(cfg, dev)
+        d = offline.device_layer(cfg, tables, w, np.zeros(cfg.V, np.int32), dev)
+        prof_x = wl.make_prof_x(cfg, dev)
+        self.prof = offline.profile_routing(cfg, d, prof_x, tables.prof_tok)
+        del prof_x
+        epg = cfg.E // cfg.P
+        d["lut"] = offline.lut_of_grouping(cfg, *self.prof, np.arange(cfg.E, dtype=np.int32) // epg)
+        self.blocked = blocked = int(blocked_weights and cfg.dtype == "bf16")
+        self.c = c = moe.make_cfg(cfg, fuse_gather=fuse_gather, weights_blocked=blocked)
+        self.fuse_gather = fuse_gather
+        if blocked:
+            # one-time layout step, like the slot permutation: not part of the layer step
+            for which, k13, k2 in ((moe.MOE_FFN_ROUTED, "W13", "W2"), (moe.MOE_FFN_SHARED, "Wsh13", "Wsh2")):
+                if d.get(k13) is None:
+                    continue
+                b13, b2 = torch.empty_like(d[k13]), torch.empty_like(d[k2])
+                moe.moe_pack_weights(c, which, d[k13], d[k2], b13, b2)
+                d[k13], d[k2] = b13, b2
+            torch.cuda.synchronize()
+        self.d = d
+        self.ws = moe.workspace(c)
+        T, E, P = cfg.T, cfg.E, cfg.P
+        self.tok = torch.as_tensor(tables.tok, device=dev)
+        self.k_tok = None if tables.k_tok is None else torch.as_tensor(tables.k_tok, device=dev)
+        self.out = torch.empty((T, cfg.H), dtype=torch.bfloat16 if cfg.dtype == "bf16" else torch.float32,
+                               device=dev)
+        self.row_ptr = torch.empty(T + 1, dtype=torch.int32, device=dev)
+        self.pair = torch.empty(P * P, dtype=torch.int32, device=dev)
+        self.ecount = torch.empty(E, dtype=torch.int32, device=dev)
+        self.topk_slot = torch.empty(T * cfg.k, dtype=torch.int32, device=dev)
+        self.W = moe.weights_struct(d)
+        self.X = moe.inputs_struct(self.x, self.tok, self.k_tok)
+
+    def run(self, steps, warmup, n_bd):
+        """W warm-ups, K timed steps (events around GEMM1 only), then a
+        breakdown pass with events around every stage."""
+        import numpy as np
+        import torch
+        from token_routing_shuffle_amd import moe
+        stream = torch.cuda.current_stream()
+        up = moe.STAGES.index("ffn_up")
+
+        def make_events(stages):
+            evs = [torch.cuda.Event(enable_timing=True) if i // 2 in stages else None
+                   for i in range(2 * moe.MOE_NSTAGES)]
+            for e in evs:
+                if e is not None:
+                    e.record(stream)
+            return evs
+
+        base_ex = dict(row_ptr=self.row_ptr, pair_count=self.pair, expert_count=self.ecount,
+                       topk_slot=self.topk_slot)
+        for _ in range(warmup):
+            moe.moe_forward(self.c, self.W, self.X, self.out, moe.exports_struct(base_ex), self.ws)
+        torch.cuda.synchronize()
+        ev_sets = [make_events({up}) for _ in range(steps)]
+        exs = [moe.exports_struct(base_ex, events=ev_sets[i]) for i in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            moe.moe_forward(self.c, self.W, self.X, self.out, exs[i], self.ws)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ms_per_step = (t1 - t0) * 1e3 / steps
+        up_ms = float(np.mean([ev_sets[i][2 * up].elapsed_time(ev_sets[i][2 * up + 1])
+                               for i in range(steps)]))
+        bd_sets = [make_events(set(range(moe.MOE_NSTAGES))) for _ in range(n_bd)]
+        bd_exs = [moe.exports_struct(base_ex, events=bd_sets[i]) for i in range(n_bd)]
+        torch.cuda.synchronize()
+        for i in range(n_bd):
+            moe.moe_forward(self.c, self.W, self.X, self.out, bd_exs[i], self.ws)
+        torch.cuda.synchronize()
+        stage_ms = {}
+        for si, name in enumerate(moe.STAGES):
+            v = [bd_sets[i][2 * si].elapsed_time(bd_sets[i][2 * si + 1]) for i in range(n_bd)]
+            stage_ms[name] = float(np.mean(v))
+        cfg = self.cfg
+        A = int(self.row_ptr[cfg.T].item())
+        counts = self.ecount.cpu().numpy()
+        pc = self.pair.cpu().numpy().reshape(cfg.P, cfg.P)
+        return dict(ms_per_step=ms_per_step, up_ms=up_ms, stage_ms=stage_ms, A=A, counts=counts,
+                    n_touched=int((counts > 0).sum()),
+                    lar=float(np.trace(pc)) / max(A, 1),
+                    load=float(counts.max() / max(counts.mean(), 1e-9)), n_bd=n_bd)
+
+
+def other_layer(name, args):
+    """One more layer shape of the workload set, built and timed like the
+    headline layer with fewer steps; its stages against their rooflines and
+    the dispatch stage as a call of its own."""
+    import torch
+    from token_routing_shuffle_amd import moe
+    from token_routing_shuffle_amd import workload as wl
+    cfg = wl.CONFIGS[name]
+    L = Layer(cfg, args, args.fuse_gather, args.blocked_weights)
+    r = L.run(args.other_steps, 10, min(args.other_steps, 20))
+    alg = algorithmic(cfg, r["A"], r["n_touched"])
+    res = {"workload": describe(cfg), "value": round(cfg.T * 1e3 / r["ms_per_step"], 1), "unit": "tokens/s",
+           "ms_per_step": round(r["ms_per_step"], 4), "steps": args.other_steps, "assignments": r["A"],
+           "lar": round(r["lar"], 4), "max_over_mean_expert_load": round(r["load"], 3),
+           "stages_ms": {k: round(v, 4) for k, v in r["stage_ms"].items()}}
+    if cfg.dtype == "bf16":
+        res["ffn_up_roofline"] = binding_roofline(alg["ffn_up_flops"], alg["ffn_up_bytes"], r["up_ms"])
+        res["stage_roofline"] = stage_rooflines(cfg, r["A"], alg, r["stage_ms"], r["up_ms"])
+    res["dispatch"] = time_dispatch(cfg, L.c, L.d, L.x, L.tok, L.row_ptr, L.topk_slot, L.ws, r["A"], args,
+                                    torch, moe, "cuda")
+    del L
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
 
 def main():
@@ -72,123 +258,53 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
+    import numpy as np  # noqa: F401
     import torch
-    from token_routing_shuffle_amd import moe, offline
+    from token_routing_shuffle_amd import moe
     from token_routing_shuffle_amd import workload as wl
 
     dev = "cuda"
     cfg = wl.CONFIGS[args.workload]
-    tables = wl.make_tables(cfg)
-    w = wl.make_weights(cfg, dev)
-    x = wl.make_x(cfg, dev)
-    # offline: placement (slot-ordered weights) and token->group LUT from a
-    # 65536-token profiling draw routed by the library itself
-    d = offline.device_layer(cfg, tables, w, np.zeros(cfg.V, np.int32), dev)
-    prof_x = wl.make_prof_x(cfg, dev)
-    prof = offline.profile_routing(cfg, d, prof_x, tables.prof_tok)
-    del prof_x
-    epg = cfg.E // cfg.P
-    d["lut"] = offline.lut_of_grouping(cfg, *prof, np.arange(cfg.E, dtype=np.int32) // epg)
-    blocked = int(args.blocked_weights and cfg.dtype == "bf16")
-    c = moe.make_cfg(cfg, fuse_gather=args.fuse_gather, weights_blocked=blocked)
-    if blocked:
-        # one-time layout step, like the slot permutation: not part of the layer step
-        for which, k13, k2 in ((moe.MOE_FFN_ROUTED, "W13", "W2"), (moe.MOE_FFN_SHARED, "Wsh13", "Wsh2")):
-            if d.get(k13) is None:
-                continue
-            b13, b2 = torch.empty_like(d[k13]), torch.empty_like(d[k2])
-            moe.moe_pack_weights(c, which, d[k13], d[k2], b13, b2)
-            d[k13], d[k2] = b13, b2
-        torch.cuda.synchronize()
-    ws = moe.workspace(c)
-    T, E, P = cfg.T, cfg.E, cfg.P
-    tok = torch.as_tensor(tables.tok, device=dev)
-    k_tok = None if tables.k_tok is None else torch.as_tensor(tables.k_tok, device=dev)
-    out = torch.empty((T, cfg.H), dtype=torch.bfloat16 if cfg.dtype == "bf16" else torch.float32,
-                      device=dev)
-    row_ptr = torch.empty(T + 1, dtype=torch.int32, device=dev)
-    pair = torch.empty(P * P, dtype=torch.int32, device=dev)
-    ecount = torch.empty(E, dtype=torch.int32, device=dev)
-    W = moe.weights_struct(d)
-    X = moe.inputs_struct(x, tok, k_tok)
-    stream = torch.cuda.current_stream()
-
-    up = moe.STAGES.index("ffn_up")
-
-    def make_events(stages):
-        evs = [torch.cuda.Event(enable_timing=True) if i // 2 in stages else None
-               for i in range(2 * moe.MOE_NSTAGES)]
-        for e in evs:
-            if e is not None:
-                e.record(stream)
-        return evs
-
-    topk_slot = torch.empty(T * cfg.k, dtype=torch.int32, device=dev)
-    base_ex = dict(row_ptr=row_ptr, pair_count=pair, expert_count=ecount, topk_slot=topk_slot)
-    for _ in range(args.warmup):
-        moe.moe_forward(c, W, X, out, moe.exports_struct(base_ex), ws)
-    torch.cuda.synchronize()
-    # timed steps: events only around GEMM1 (each event pair costs GPU time)
-    ev_sets = [make_events({up}) for _ in range(args.steps)]
-    exs = [moe.exports_struct(base_ex, events=ev_sets[i]) for i in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        moe.moe_forward(c, W, X, out, exs[i], ws)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_per_step = (t1 - t0) * 1e3 / args.steps
-    up_timed_ms = float(np.mean([ev_sets[i][2 * up].elapsed_time(ev_sets[i][2 * up + 1])
-                                 for i in range(args.steps)]))
-    # stage breakdown: a further untimed pass with events around every stage
-    n_bd = min(args.steps, 50)
-    bd_sets = [make_events(set(range(moe.MOE_NSTAGES))) for _ in range(n_bd)]
-    bd_exs = [moe.exports_struct(base_ex, events=bd_sets[i]) for i in range(n_bd)]
-    torch.cuda.synchronize()
-    for i in range(n_bd):
-        moe.moe_forward(c, W, X, out, bd_exs[i], ws)
-    torch.cuda.synchronize()
-    stage_ms = {}
-    for si, name in enumerate(moe.STAGES):
-        v = [bd_sets[i][2 * si].elapsed_time(bd_sets[i][2 * si + 1]) for i in range(n_bd)]
-        stage_ms[name] = float(np.mean(v))
+    L = Layer(cfg, args, args.fuse_gather, args.blocked_weights)
+    T = cfg.T
+    r = L.run(args.steps, args.warmup, min(args.steps, 50))
+    ms_per_step, up_ms, stage_ms, A = r["ms_per_step"], r["up_ms"], r["stage_ms"], r["A"]
 
     if args.copy_calib_mb > 0:
         copy_calibration(args.copy_calib_mb, torch, dev)
-    A = int(row_ptr[T].item())
-    pc = pair.cpu().numpy().reshape(P, P)
-    counts = ecount.cpu().numpy()
-    alg = algorithmic(cfg, A)
-    up_ms = up_timed_ms
-    achieved = alg["ffn_up_flops"] / (up_ms * 1e-3) / 1e12
+    alg = algorithmic(cfg, A, r["n_touched"])
     traffic, traffic_note = measured_traffic(args.workload)
-    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFLOPS, 4),
-                "traffic": traffic, "traffic_unit": "bytes per launch", "traffic_source": traffic_note,
-                "kernel": "k_grouped_gemm<true,256,256> (GEMM1 + SwiGLU, routed + shared)",
-                "flops_per_launch": alg["ffn_up_flops"], "avg_launch_ms": round(up_ms, 4)}
-    secondary = {
-        "ffn_down_tflops": round(alg["ffn_down_flops"] / (stage_ms["ffn_down"] * 1e-3) / 1e12, 2),
-        "combine_gbs": round(alg["combine_bytes"] / (stage_ms["combine"] * 1e-3) / 1e9, 1),
-        # with the gather fused into GEMM1 there is no separate dispatch copy to time
-        "dispatch_gbs": round(alg["dispatch_bytes"] /
-                              ((stage_ms["shuffle"] + stage_ms["gather"]) * 1e-3) / 1e9, 1)
-        if args.fuse_gather == 0 else None,
-    }
-    stage_roofline = stage_rooflines(cfg, A, alg, stage_ms, up_ms)
+    roofline = binding_roofline(alg["ffn_up_flops"], alg["ffn_up_bytes"], up_ms)
+    kname = "k_grouped_gemm<true,%d,%d>" % ((256, 256) if moe_wide(cfg) else (128, 384))
+    roofline.update({"traffic": traffic, "traffic_unit": "bytes per launch", "traffic_source": traffic_note,
+                     "kernel": kname + " (GEMM1 + SwiGLU, routed + shared)",
+                     "touched_experts": r["n_touched"]})
+    stage_roofline = stage_rooflines(cfg, A, alg, stage_ms, up_ms) if cfg.dtype == "bf16" else None
+    down = binding_roofline(alg["ffn_down_flops"], alg["ffn_down_bytes"], stage_ms["ffn_down"]) \
+        if cfg.dtype == "bf16" else None
 
     srs_sag = share = cosched = dispatch = None
     if not args.no_extras:
-        dispatch = time_dispatch(cfg, c, d, x, tok, row_ptr, topk_slot, ws, A, args, torch, moe, dev)
-        srs_sag = time_srs_sag(cfg, c, tables, args, torch, np, moe, wl, dev)
-        share = group_share(cfg, c, d, x, tok, row_ptr, topk_slot, ws, args, torch, np, moe, dev)
-        cosched = coschedule(cfg, c, tables, prof, tok, row_ptr, topk_slot, d["lut"], torch, np, moe,
-                             dev)
+        dispatch = time_dispatch(cfg, L.c, L.d, L.x, L.tok, L.row_ptr, L.topk_slot, L.ws, A, args, torch, moe, dev)
+        srs_sag = time_srs_sag(cfg, L.c, L.tables, args, torch, np, moe, wl, dev)
+        share = group_share(cfg, L.c, L.d, L.x, L.tok, L.row_ptr, L.topk_slot, L.ws, args, torch, np, moe, dev)
+        cosched = coschedule(cfg, L.c, L.tables, L.prof, L.tok, L.row_ptr, L.topk_slot, L.d["lut"], torch, np,
+                             moe, dev)
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, tables, w, x, np, torch, min(args.cpu_sample, cfg.T))
+        n = args.cpu_sample or CPU_SAMPLE.get(args.workload, 4096)
+        cpu = cpu_baseline(cfg, L.tables, L.w, L.x, np, torch, min(n, T))
+    del L
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+    others = None
+    if not args.no_extras and not args.no_other_layers:
+        others = {}
+        for name in OTHER_LAYERS:
+            if name != args.workload:
+                others[name] = other_layer(name, args)
 
     res = {
         "metric": "MoE-layer tokens/s on 1 MI355X",
@@ -203,28 +319,32 @@ def main():
         "vs_baseline": None,
         "dtype": cfg.dtype,
         "data": "synthetic (seeded; Zipf token IDs, N(0,1) activations, N(0,1/fan_in) weights)",
-        "config": {"workload": "DeepSeek-V2-Lite-shaped MoE layer: T=%d H=%d E=%d top-%d softmax "
-                               "+%d shared, I=%d, P=%d, V=%d" % (T, cfg.H, E, cfg.k, cfg.n_shared,
-                                                                 cfg.I, P, cfg.V)
-                   if args.workload == "dsv2lite" else args.workload,
+        "config": {"workload": describe(cfg), "name": cfg.name,
                    "tokens": T, "assignments": A, "fuse_gather": args.fuse_gather,
-                   "weights_blocked": blocked,
-                   "lar": round(float(np.trace(pc)) / max(A, 1), 4),
-                   "max_over_mean_expert_load": round(float(counts.max() / max(counts.mean(), 1e-9)), 3)},
+                   "weights_blocked": int(args.blocked_weights and cfg.dtype == "bf16"),
+                   "lar": round(r["lar"], 4),
+                   "max_over_mean_expert_load": round(r["load"], 3)},
         "stages_ms": {k: round(v, 4) for k, v in stage_ms.items()},
         "stages_source": "separate pass of %d steps with HIP events around every stage "
                          "(each event pair adds GPU time; ffn_up in the timed steps: %.4f ms)"
-                         % (n_bd, up_timed_ms),
-        "secondary": secondary,
+                         % (r["n_bd"], up_ms),
         "stage_roofline": stage_roofline,
+        "ffn_down_roofline": down,
         "roofline": roofline,
         "dispatch": dispatch,
         "srs_sag": srs_sag,
         "group_share": share,
         "coschedule": cosched,
+        "other_layers": others,
         "cpu_baseline": cpu,
     }
     print(json.dumps(res), flush=True)
+
+
+def moe_wide(cfg):
+    """256-wide GEMM1 tiles (2I and the shared 2*ns*Is multiples of 256)."""
+    Ish = cfg.n_shared * cfg.I_shared
+    return (2 * cfg.I) % 256 == 0 and (Ish == 0 or (2 * Ish) % 256 == 0)
 
 
 MALL_BYTES = 256 << 20
@@ -487,10 +607,51 @@ def measured_traffic(workload):
         return None, "counter summary unreadable"
 
 
+class _HostExperts:
+    """Host copies of single experts of a device weight stack [E, ...],
+    fetched once each on first use (bf16 as uint16 bit patterns): the
+    oracle's expert loop indexes the stack by original expert id, and a
+    bounded token sample touches only a few of the 22.6 GB of experts of the
+    largest layer."""
+
+    def __init__(self, t, host):
+        self.t, self.host, self.cache = t, host, {}
+
+    def __getitem__(self, e):
+        e = int(e)
+        if e not in self.cache:
+            self.cache[e] = self.host(self.t[e])
+        return self.cache[e]
+
+    def prefetch(self, ids):
+        for e in ids:
+            self[e]
+
+
+def cpu_info():
+    """Logical CPUs this process may run on, and the CPU model."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return n, model
+
+
 def cpu_baseline(cfg, tables, w, x, np, torch, n_sample):
     """The oracle (unchanged) on a bounded sample of the same layer: gate
     logits, routing, dispatch metadata and the dense per-token MoE for the
-    first n_sample tokens; tokens/s = n_sample / wall time."""
+    first n_sample tokens, repeated in whole passes until at least 10 s of
+    CPU work; tokens/s = passes * n_sample / wall time.  The expert weights
+    the sample routes to are copied to the host before the timing."""
     from oracle import moe_oracle as mo
 
     def h(t):
@@ -501,22 +662,31 @@ def cpu_baseline(cfg, tables, w, x, np, torch, n_sample):
             return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
         return t.cpu().numpy()
 
-    hw = {k: h(v) for k, v in w.items()}
-    xs = h(x)[:n_sample]
+    hw = {k: h(v) for k, v in w.items() if k not in ("W13", "W2")}
+    W13, W2 = _HostExperts(w["W13"], h), _HostExperts(w["W2"], h)
+    xs = h(x[:n_sample])
     tok = tables.tok[:n_sample]
     k_tok = None if tables.k_tok is None else tables.k_tok[:n_sample]
-    def one_pass():
+
+    def route():
         l64 = mo.logits(xs, hw["Wg"], tok, tables.pref, cfg.aff_bias if tables.pref is not None else 0.0)
-        sel, wt = mo.route(l64, cfg, k_tok, tables.ebias)
+        return mo.route(l64, cfg, k_tok, tables.ebias)
+
+    sel0, _ = route()
+    used = np.unique(sel0[sel0 >= 0])
+    W13.prefetch(used)
+    W2.prefetch(used)
+
+    def one_pass():
+        sel, wt = route()
         kt = k_tok if k_tok is not None else np.full(n_sample, cfg.k)
         rp = mo.row_ptr_of(kt)
         slot = tables.perm[sel[sel >= 0]]
         lut = np.arange(cfg.V, dtype=np.int32) % cfg.P
         mo.shuffle(rp, slot, tok, lut, cfg.E, cfg.P)
-        mo.moe_output(xs, sel, wt, hw["W13"], hw["W2"], cfg.I, hw.get("Wsh13"), hw.get("Wsh2"),
+        mo.moe_output(xs, sel, wt, W13, W2, cfg.I, hw.get("Wsh13"), hw.get("Wsh2"),
                       cfg.n_shared, cfg.I_shared)
 
-    # whole passes over the sample until at least 10 s of CPU work (at most 30 passes)
     passes = 0
     t0 = time.perf_counter()
     while True:
@@ -531,11 +701,14 @@ def cpu_baseline(cfg, tables, w, x, np, torch, n_sample):
         threads = max([1] + [i.get("num_threads", 1) for i in threadpool_info()])
     except Exception:
         pass
-    return {"value": round(passes * n_sample / dt, 2), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle", "wall_s": round(dt, 2),
+    nproc, model = cpu_info()
+    return {"value": round(passes * n_sample / dt, 3), "unit": "tokens/s", "cores": threads,
+            "nproc": nproc, "cpu_model": model, "kind": "oracle", "wall_s": round(dt, 2),
             "sample": "%d passes over the first %d of %d tokens of the same layer (fp64 numpy "
                       "oracle: logits, routing, dispatch metadata with a v mod P lookup table, "
-                      "dense per-token MoE incl. shared experts)" % (passes, n_sample, cfg.T)}
+                      "dense per-token MoE incl. shared experts; %d routed experts touched); "
+                      "cores = the BLAS threads numpy's matrix products use (the rest of the "
+                      "oracle is single-threaded numpy)" % (passes, n_sample, cfg.T, len(used))}
 
 
 if __name__ == "__main__":

@@ -43,6 +43,42 @@ def test_stage_rooflines_fractions():
     assert 0 < r["route"]["mfma_frac"] < r["route"]["frac"] < 1
 
 
+def test_binding_roofline_of_the_headline_layer():
+    """DeepSeek-V3-shaped prefill GEMM1: 15.5 GB of algorithmic bytes (all
+    256 experts' W1/W3, the shared W1/W3, x once, the SwiGLU outputs) take
+    1.94 ms at 8 TB/s, longer than its 4.33 TFLOP at 2.5 PFLOP/s (1.73 ms):
+    HBM is the binding roof."""
+    cfg = wl.CONFIGS["dsv3_prefill"]
+    A = cfg.T * cfg.k
+    alg = bench.algorithmic(cfg, A)
+    T, H, I, Ish, E = cfg.T, cfg.H, cfg.I, cfg.I_shared, cfg.E
+    assert alg["ffn_up_bytes"] == 2 * (E * 2 * I * H + 2 * Ish * H + T * H + A * I + T * Ish)
+    r = bench.binding_roofline(alg["ffn_up_flops"], alg["ffn_up_bytes"], 4.9)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s" and r["peak"] == bench.HBM_PEAK_GBS
+    assert r["roof_ms"] == pytest.approx(alg["ffn_up_bytes"] / 8e12 * 1e3, rel=1e-3)
+    assert r["frac"] == pytest.approx(r["roof_ms"] / 4.9, rel=1e-3)
+    assert r["mfma_frac"] < r["frac"]
+    # fewer touched experts, fewer weight bytes
+    assert bench.algorithmic(cfg, A, 200)["ffn_up_bytes"] < alg["ffn_up_bytes"]
+    # the DeepSeek-V2-Lite-shaped layer's GEMM1 is MFMA-bound
+    c2 = wl.CONFIGS["dsv2lite"]
+    a2 = bench.algorithmic(c2, c2.T * c2.k)
+    assert bench.binding_roofline(a2["ffn_up_flops"], a2["ffn_up_bytes"], 0.37)["bound"] == "mfma"
+
+
+def test_default_workload_is_the_largest_layer():
+    assert bench.parse([]).workload == "dsv3_prefill"
+    big = max(wl.CONFIGS.values(), key=lambda c: bench.algorithmic(c, c.T * c.k)["ffn_up_flops"])
+    assert big.name == bench.WORKLOAD
+    assert "DeepSeek-V3-shaped" in bench.describe(big) and "T=8192" in bench.describe(big)
+    assert set(bench.OTHER_LAYERS) | {bench.WORKLOAD} == set(wl.CONFIGS)
+
+
+def test_cpu_info():
+    n, model = bench.cpu_info()
+    assert n >= 1 and isinstance(model, str) and model
+
+
 def test_more_than_one_gpu_is_refused():
     p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)

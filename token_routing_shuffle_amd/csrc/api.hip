@@ -234,16 +234,14 @@ MOE_API int32_t moe_route(const moe_cfg* cfg, const void* x, const void* Wg, con
     return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_route");
 }
 
-MOE_API int32_t moe_shuffle(const moe_cfg* cfg, const int32_t* row_ptr, const int32_t* topk_slot,
-                            const int32_t* tok, const int32_t* lut, const void* x,
-                            int32_t* expert_count, int32_t* expert_off, int32_t* group_count,
-                            int32_t* group_off, int32_t* pair_count, int32_t* tok_perm,
-                            int32_t* tok_off, int32_t* sorted_to_assign, int32_t* assign_to_sorted,
-                            void* x_sorted, void* ws, size_t ws_bytes, void* stream)
+// Argument checks shared by moe_shuffle and moe_shuffle_noalloc.
+static int32_t check_shuffle_args(const moe_cfg& c, const int32_t* row_ptr, const int32_t* topk_slot,
+                                  const int32_t* tok, const int32_t* lut, const void* x,
+                                  int32_t* expert_count, int32_t* expert_off, int32_t* group_count,
+                                  int32_t* group_off, int32_t* pair_count, int32_t* tok_perm,
+                                  int32_t* tok_off, int32_t* sorted_to_assign, int32_t* assign_to_sorted,
+                                  void* x_sorted)
 {
-    int32_t rc = check_cfg(cfg);
-    if (rc != MOE_OK) return rc;
-    const moe_cfg& c = *cfg;
     REQUIRE(row_ptr);
     REQUIRE(expert_count);
     REQUIRE(expert_off);
@@ -264,10 +262,15 @@ MOE_API int32_t moe_shuffle(const moe_cfg* cfg, const int32_t* row_ptr, const in
         REQUIRE16(x);
         REQUIRE16(x_sorted);
     }
-    const WsLayout L = ws_layout(c);
-    rc = check_ws(ws, ws_bytes, L.shuffle_need);
-    if (rc != MOE_OK) return rc;
+    return MOE_OK;
+}
+
+static ShuffleOut shuffle_outputs(int32_t* expert_count, int32_t* expert_off, int32_t* group_count,
+                                  int32_t* group_off, int32_t* pair_count, int32_t* tok_perm,
+                                  int32_t* tok_off, int32_t* sorted_to_assign, int32_t* assign_to_sorted)
+{
     ShuffleOut o;
+    memset(&o, 0, sizeof(o));
     o.expert_count = expert_count;
     o.expert_off = expert_off;
     o.group_count = group_count;
@@ -277,14 +280,36 @@ MOE_API int32_t moe_shuffle(const moe_cfg* cfg, const int32_t* row_ptr, const in
     o.tok_off = tok_off;
     o.s2a = sorted_to_assign;
     o.a2s = assign_to_sorted;
-    o.row_tok = at<int32_t>(ws, L.row_tok);
+    o.row_tok = nullptr;
+    o.gemm_ctr = nullptr;
+    return o;
+}
+
+MOE_API int32_t moe_shuffle(const moe_cfg* cfg, const int32_t* row_ptr, const int32_t* topk_slot,
+                            const int32_t* tok, const int32_t* lut, const void* x,
+                            int32_t* expert_count, int32_t* expert_off, int32_t* group_count,
+                            int32_t* group_off, int32_t* pair_count, int32_t* tok_perm,
+                            int32_t* tok_off, int32_t* sorted_to_assign, int32_t* assign_to_sorted,
+                            void* x_sorted, void* ws, size_t ws_bytes, void* stream)
+{
+    int32_t rc = check_cfg(cfg);
+    if (rc != MOE_OK) return rc;
+    const moe_cfg& c = *cfg;
+    rc = check_shuffle_args(c, row_ptr, topk_slot, tok, lut, x, expert_count, expert_off, group_count,
+                            group_off, pair_count, tok_perm, tok_off, sorted_to_assign, assign_to_sorted,
+                            x_sorted);
+    if (rc != MOE_OK) return rc;
+    const WsLayout L = ws_layout(c);
+    rc = check_ws(ws, ws_bytes, L.shuffle_need);
+    if (rc != MOE_OK) return rc;
+    ShuffleOut o = shuffle_outputs(expert_count, expert_off, group_count, group_off, pair_count, tok_perm,
+                                   tok_off, sorted_to_assign, assign_to_sorted);
     o.g_pred = at<int32_t>(ws, L.g_pred);
     o.hist = at<int32_t>(ws, L.hist);
     o.thist = at<int32_t>(ws, L.thist);
     o.rowtot = at<int32_t>(ws, L.rowtot);
     o.bstart = at<int32_t>(ws, L.bstart);
     o.tstart = at<int32_t>(ws, L.tstart);
-    o.gemm_ctr = nullptr;
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_shuffle(c, L.nb, L.tpb, row_ptr, topk_slot, tok, lut, o, s);
     if (e == hipSuccess && x_sorted != nullptr) e = launch_gather(c, x, row_ptr, assign_to_sorted, x_sorted, s);
