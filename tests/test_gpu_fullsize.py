@@ -91,6 +91,6 @@ def test_max_tokens():
     from token_routing_shuffle_amd import moe
     T = 262144
     c = hn.make_case("dsv2lite", T=T, profile_tokens=65536)
-    assert T * c.cfg.k * c.cfg.H * 2 > 3 * 2 ** 31
+    assert T * c.cfg.k * c.cfg.H * 2 > 2 ** 32
     assert moe.moe_validate(moe.make_cfg(c.cfg)) == moe.MOE_OK
     _check(c, fuse=0)
