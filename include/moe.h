@@ -217,6 +217,29 @@ int32_t moe_shuffle(const moe_cfg* cfg, const int32_t* row_ptr, const int32_t* t
                     void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_shuffle without a workspace, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Arguments, results and errors as moe_shuffle without
+ * ws / ws_bytes.  Its scratch -- the predicted groups g_pred [T], the
+ * per-block histograms [E*P][nb] and [P][nb] (nb = ceil(T / tpb) blocks of
+ * tpb = 64..256 tokens), the row totals and the bucket and group starts --
+ * lives in a static device array of MOE_NOALLOC_SCRATCH_BYTES that every GPU
+ * the library runs on holds until the process ends; a layer that needs more
+ * is rejected with MOE_EWORKSPACE before anything is enqueued.  Every kernel
+ * overwrites the scratch it reads, so nothing needs clearing between calls,
+ * but all calls on one GPU share the array: calls that overlap on one GPU
+ * (other streams, other host threads) race.  Allocates nothing: no hipMalloc,
+ * no hipFree, no allocating library routine.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+int32_t moe_shuffle_noalloc(const moe_cfg* cfg, const int32_t* row_ptr, const int32_t* topk_slot,
+                            const int32_t* tok, const int32_t* lut, const void* x,
+                            int32_t* expert_count, int32_t* expert_off, int32_t* group_count,
+                            int32_t* group_off, int32_t* pair_count, int32_t* tok_perm,
+                            int32_t* tok_off, int32_t* sorted_to_assign, int32_t* assign_to_sorted,
+                            void* x_sorted, void* stream);
+
+/*
  * Expert FFN (grouped SwiGLU GEMMs on MFMA).  Passages: each device runs the
  * experts placed on it over the rows shuffled to it (Semantic Parallelism,
  * ja technical overview §2.2A-B) -- one placement group's slot range is one

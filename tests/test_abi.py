@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
         "moe_route_workspace_bytes",
         "moe_token_group_counts", "moe_lut_from_counts", "moe_expert_group_counts",
         "moe_balanced_assign", "moe_optimize_placement", "moe_request_group_hist",
-        "moe_sigmoid", "moe_pack_weights"])
+        "moe_sigmoid", "moe_pack_weights", "moe_shuffle_noalloc"])
 
 
 def test_library_exports_every_declared_symbol(m):

@@ -12,7 +12,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libmoe.so")
-SOURCES = ["api.hip", "route.hip", "shuffle.hip", "ffn.hip", "combine.hip", "srs_sag.hip", "cosched.hip"]
+SOURCES = ["api.hip", "route.hip", "shuffle.hip", "ffn.hip", "combine.hip", "srs_sag.hip", "cosched.hip", "noalloc.hip"]
 HEADERS = ["common.h", "internal.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -316,6 +316,60 @@ MOE_API int32_t moe_shuffle(const moe_cfg* cfg, const int32_t* row_ptr, const in
     return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_shuffle");
 }
 
+// Scratch of the shuffle alone, packed from offset 0: g_pred [T], the
+// per-block histograms hist [E*P][nb] and thist [P][nb], row totals, bucket
+// and group starts (256-byte aligned sections).  Returns the bytes needed.
+static size_t shuffle_scratch(const moe_cfg& c, ShuffleOut& o, char* base, int* nb, int* tpb)
+{
+    *tpb = shuffle_tpb(c.T, c.E, c.P);
+    *nb = std::max(1, ceil_div(c.T, *tpb));
+    const size_t E = c.E, P = c.P, NB = (size_t)*nb;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        int32_t* p = (int32_t*)(base + off);
+        off += (bytes + 255) & ~(size_t)255;
+        return p;
+    };
+    o.g_pred = take((size_t)c.T * 4);
+    o.hist = take(E * P * NB * 4);
+    o.thist = take(P * NB * 4);
+    o.rowtot = take((E * P + P) * 4);
+    o.bstart = take((E * P + 1) * 4);
+    o.tstart = take((P + 1) * 4);
+    return off;
+}
+
+MOE_API int32_t moe_shuffle_noalloc(const moe_cfg* cfg, const int32_t* row_ptr, const int32_t* topk_slot,
+                                    const int32_t* tok, const int32_t* lut, const void* x,
+                                    int32_t* expert_count, int32_t* expert_off, int32_t* group_count,
+                                    int32_t* group_off, int32_t* pair_count, int32_t* tok_perm,
+                                    int32_t* tok_off, int32_t* sorted_to_assign, int32_t* assign_to_sorted,
+                                    void* x_sorted, void* stream)
+{
+    int32_t rc = check_cfg(cfg);
+    if (rc != MOE_OK) return rc;
+    const moe_cfg& c = *cfg;
+    rc = check_shuffle_args(c, row_ptr, topk_slot, tok, lut, x, expert_count, expert_off, group_count,
+                            group_off, pair_count, tok_perm, tok_off, sorted_to_assign, assign_to_sorted,
+                            x_sorted);
+    if (rc != MOE_OK) return rc;
+    ShuffleOut o = shuffle_outputs(expert_count, expert_off, group_count, group_off, pair_count, tok_perm,
+                                   tok_off, sorted_to_assign, assign_to_sorted);
+    int nb = 0, tpb = 0;
+    const size_t need = shuffle_scratch(c, o, nullptr, &nb, &tpb);
+    if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
+        return fail(MOE_EWORKSPACE, "moe_shuffle_noalloc: layer needs %zu bytes of scratch, the static "
+                    "array holds %zu", need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+    void* base = nullptr;
+    hipError_t e = noalloc_scratch(&base);
+    if (e != hipSuccess) return hip_fail(e, "moe_shuffle_noalloc (scratch address)");
+    shuffle_scratch(c, o, (char*)base, &nb, &tpb);
+    hipStream_t s = (hipStream_t)stream;
+    e = launch_shuffle(c, nb, tpb, row_ptr, topk_slot, tok, lut, o, s);
+    if (e == hipSuccess && x_sorted != nullptr) e = launch_gather(c, x, row_ptr, assign_to_sorted, x_sorted, s);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_shuffle_noalloc");
+}
+
 MOE_API int32_t moe_expert_ffn(const moe_cfg* cfg, int32_t which, const void* x_sorted,
                                const void* x, const int32_t* row_ptr,
                                const int32_t* sorted_to_assign, const int32_t* expert_off,

@@ -62,6 +62,11 @@ struct ShuffleOut {
     int32_t* gemm_ctr;  // [16] grouped-GEMM tile counters to zero, or nullptr
 };
 hipError_t launch_sigmoid(const float* x, float* y, int64_t n, hipStream_t s);
+
+// This device's copy of the static scratch array of moe_shuffle_noalloc
+// (MOE_NOALLOC_SCRATCH_BYTES, 256-byte aligned); its address is looked up
+// once per device.
+hipError_t noalloc_scratch(void** out);
 hipError_t launch_shuffle(const moe_cfg& c, int nb, int tpb, const int32_t* row_ptr,
                           const int32_t* topk_slot, const int32_t* tok, const int32_t* lut,
                           const ShuffleOut& o, hipStream_t s);

@@ -85,6 +85,8 @@ def _load():
     lib.moe_route.argtypes = [P(moe_cfg)] + [vp] * 11 + [vp, sz, vp]
     lib.moe_shuffle.restype = i32
     lib.moe_shuffle.argtypes = [P(moe_cfg)] + [vp] * 15 + [vp, sz, vp]
+    lib.moe_shuffle_noalloc.restype = i32
+    lib.moe_shuffle_noalloc.argtypes = [P(moe_cfg)] + [vp] * 15 + [vp]
     lib.moe_expert_ffn.restype = i32
     lib.moe_expert_ffn.argtypes = [P(moe_cfg), i32] + [vp] * 7 + [i32, i32, vp, vp, sz, vp]
     lib.moe_combine.restype = i32
@@ -127,7 +129,7 @@ def lib():
 
 
 EXPORTED = ("moe_validate", "moe_workspace_bytes", "moe_route_workspace_bytes", "moe_last_error",
-            "moe_route", "moe_shuffle",
+            "moe_route", "moe_shuffle", "moe_shuffle_noalloc",
             "moe_expert_ffn", "moe_combine", "moe_forward", "moe_srs", "moe_sag",
             "moe_token_group_counts", "moe_lut_from_counts", "moe_expert_group_counts",
             "moe_balanced_assign", "moe_optimize_placement", "moe_request_group_hist",
@@ -225,6 +227,18 @@ def moe_shuffle(cfg, row_ptr, topk_slot, tok, lut, x, expert_count, expert_off, 
                            _p(pair_count), _p(tok_perm), _p(tok_off), _p(sorted_to_assign),
                            _p(assign_to_sorted), _p(x_sorted), wp, wb, _stream(stream))
     _check(rc, "moe_shuffle")
+
+
+def moe_shuffle_noalloc(cfg, row_ptr, topk_slot, tok, lut, x, expert_count, expert_off, group_count,
+                        group_off, pair_count, tok_perm, tok_off, sorted_to_assign, assign_to_sorted,
+                        x_sorted=None, stream=None):
+    """moe_shuffle with its scratch in the library's static device array
+    (no workspace; nothing allocated)."""
+    rc = lib().moe_shuffle_noalloc(ctypes.byref(cfg), _p(row_ptr), _p(topk_slot), _p(tok), _p(lut), _p(x),
+                                   _p(expert_count), _p(expert_off), _p(group_count), _p(group_off),
+                                   _p(pair_count), _p(tok_perm), _p(tok_off), _p(sorted_to_assign),
+                                   _p(assign_to_sorted), _p(x_sorted), _stream(stream))
+    _check(rc, "moe_shuffle_noalloc")
 
 
 def moe_expert_ffn(cfg, which, x_sorted, x, row_ptr, sorted_to_assign, expert_off, W13, W2,
