@@ -13,8 +13,9 @@
 // counts and offsets, the P x P would-be all-to-all matrix and the token
 // permutation.
 //
-// Three kernels: per-block LDS histograms; a wave per bucket that turns its
-// row of per-block counts into offsets within the bucket (and the bucket's
+// Three kernels: per-block LDS histograms, stored block-major (one
+// contiguous row of bucket counts per block); a column scan that turns each
+// bucket's per-block counts into offsets within the bucket (and the bucket's
 // total); a scatter whose blocks each scan the bucket totals (E*P of them)
 // into bucket starts in LDS (block 0 also writes the per-slot / per-group
 // results; an empty layer runs that scan as a kernel of its own) and rank
@@ -55,34 +56,75 @@ __global__ __launch_bounds__(kThreads) void k_hist(ShParams p)
         p.o.g_pred[t] = g;
         atomicAdd(&tcnt[g], 1);
         const int a0 = p.row_ptr[t], a1 = p.row_ptr[t + 1];
-        for (int a = a0; a < a1; ++a) {
-            const int s = clampi(p.slot[a], 0, p.E - 1);
-            atomicAdd(&cnt[s * p.P + g], 1);
+        // eight slot loads in flight before their counts are added (one
+        // dependent load per atomic would serialise k_t memory latencies)
+        for (int a = a0; a < a1; a += 8) {
+            int s[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) s[q] = a + q < a1 ? p.slot[a + q] : -1;
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                if (a + q < a1) atomicAdd(&cnt[clampi(s[q], 0, p.E - 1) * p.P + g], 1);
         }
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < p.nbk; i += kThreads) p.o.hist[(size_t)i * p.nb + b] = cnt[i];
-    if (threadIdx.x < p.P) p.o.thist[threadIdx.x * p.nb + b] = tcnt[threadIdx.x];
+    // block-major tables: block b's counts are one contiguous row
+    for (int i = threadIdx.x; i < p.nbk; i += kThreads) p.o.hist[(size_t)b * p.nbk + i] = cnt[i];
+    if (threadIdx.x < p.P) p.o.thist[(size_t)b * p.P + threadIdx.x] = tcnt[threadIdx.x];
 }
 
-// Rows of the count tables (buckets, then predicted groups): one wave per
-// row turns the row's per-block counts into exclusive offsets in place and
-// stores the row total.
+// Columns of the count tables (buckets, then predicted groups) turned into
+// exclusive offsets in place, with the column totals.  A block takes 64
+// columns (one per lane: neighbouring lanes read neighbouring columns, so
+// every access to a block row is coalesced) and splits the nb block rows
+// between its four waves: each wave sums its rows, the waves' sums are
+// scanned through LDS, and each wave rewrites its rows as running offsets.
 __global__ __launch_bounds__(kThreads) void k_rowscan(ShParams p)
 {
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6);   // wave-uniform
-    const int l = threadIdx.x & 63;
-    if (row >= p.nbk + p.P) return;
-    int32_t* a = row < p.nbk ? p.o.hist + (size_t)row * p.nb : p.o.thist + (size_t)(row - p.nbk) * p.nb;
-    int carry = 0;
-    for (int base = 0; base < p.nb; base += 64) {
-        const int i = base + l;
-        const int v = i < p.nb ? a[i] : 0;
-        const int incl = wave_incl_scan(v);
-        if (i < p.nb) a[i] = carry + incl - v;
-        carry += __shfl(incl, 63);
+    __shared__ int s_part[4][64];
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int col = blockIdx.x * 64 + l;
+    const bool valid = col < p.nbk + p.P;
+    const bool bucket = col < p.nbk;
+    int32_t* a = bucket ? p.o.hist + col : p.o.thist + (col - p.nbk);
+    const size_t stride = bucket ? (size_t)p.nbk : (size_t)p.P;
+    const int per = (p.nb + 3) / 4;
+    const int r0 = min(p.nb, w * per), r1 = min(p.nb, r0 + per);
+    int sum = 0;
+    if (valid) {
+        int r = r0;
+        for (; r + 8 <= r1; r += 8) {
+            int v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = a[(size_t)(r + q) * stride];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) sum += v[q];
+        }
+        for (; r < r1; ++r) sum += a[(size_t)r * stride];
     }
-    if (l == 0) p.o.rowtot[row] = carry;
+    s_part[w][l] = sum;
+    __syncthreads();
+    int run = 0;
+    for (int q = 0; q < w; ++q) run += s_part[q][l];
+    if (valid) {
+        int r = r0;
+        for (; r + 8 <= r1; r += 8) {
+            int v[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = a[(size_t)(r + q) * stride];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                a[(size_t)(r + q) * stride] = run;
+                run += v[q];
+            }
+        }
+        for (; r < r1; ++r) {
+            const int v = a[(size_t)r * stride];
+            a[(size_t)r * stride] = run;
+            run += v;
+        }
+        if (w == 3) p.o.rowtot[col] = run;
+    }
 }
 
 // Bucket totals -> bucket starts in LDS (s_start[0..nbk], the last entry A)
@@ -92,6 +134,9 @@ MOE_DEV void bucket_starts(const ShParams& p, int* smem, int* s_start, int* s_ts
 {
     constexpr int kPer = (kMaxBuckets + NT - 1) / NT;  // buckets per thread
     const int nbk = p.nbk, P = p.P;
+    // the P group totals, one per lane of the first wave, loaded with the
+    // bucket totals and scanned in a wave
+    const int gv = threadIdx.x < P ? p.o.rowtot[nbk + threadIdx.x] : 0;
     int v[kPer], sum = 0;
 #pragma unroll
     for (int q = 0; q < kPer; ++q) {
@@ -107,25 +152,24 @@ MOE_DEV void bucket_starts(const ShParams& p, int* smem, int* s_start, int* s_ts
         if (k < nbk) s_start[k] = run;
         run += v[q];
     }
-    if (threadIdx.x == 0) {
-        s_start[nbk] = A;
-        int t = 0;
-        for (int g = 0; g < P; ++g) {
-            s_tstart[g] = t;
-            t += p.o.rowtot[nbk + g];
-        }
-        s_tstart[P] = t;
+    if (threadIdx.x < 64) {
+        const int gi = wave_incl_scan(gv);
+        if (threadIdx.x < P) s_tstart[threadIdx.x] = gi - gv;
+        if (threadIdx.x == P - 1) s_tstart[P] = gi;
+        if (threadIdx.x == 0) s_start[nbk] = A;
     }
     __syncthreads();
 }
 
 // The per-slot / per-group results, the pair matrix and the token offsets
-// from the LDS starts; zeroes the grouped GEMMs' tile counters.
+// from the LDS starts; zeroes the grouped GEMMs' tile counters.  Called by
+// every thread of one block; s_pair is LDS scratch of P*P ints.
 template <int NT>
-MOE_DEV void write_offsets(const ShParams& p, const int* s_start, const int* s_tstart)
+MOE_DEV void write_offsets(const ShParams& p, const int* s_start, const int* s_tstart, int* s_pair)
 {
     if (p.o.gemm_ctr != nullptr && threadIdx.x < 16) p.o.gemm_ctr[threadIdx.x] = 0;
     const int E = p.E, P = p.P, epg = E / P;
+    for (int i = threadIdx.x; i < P * P; i += NT) s_pair[i] = 0;
     for (int s = threadIdx.x; s <= E; s += NT) {
         const int off = s_start[s * P];
         p.o.expert_off[s] = off;
@@ -137,13 +181,30 @@ MOE_DEV void write_offsets(const ShParams& p, const int* s_start, const int* s_t
         if (g < P) p.o.group_count[g] = s_start[(g + 1) * epg * P] - off;
         p.o.tok_off[g] = s_tstart[g];
     }
-    // pair_count[pg * P + g]: predicted group pg, expert group g
-    for (int i = threadIdx.x; i < P * P; i += NT) {
-        const int pg = i / P, g = i % P;
-        int c = 0;
-        for (int s = g * epg; s < (g + 1) * epg; ++s) c += s_start[s * P + pg + 1] - s_start[s * P + pg];
-        p.o.pair_count[i] = c;
+    __syncthreads();
+    // pair_count[pg * P + g]: predicted group pg, expert group g.  Each
+    // (pg, g) sums its epg bucket counts in `parts` interleaved pieces, one
+    // thread per piece, four bucket reads in flight; the pieces are added
+    // into LDS (at most `parts` adds per entry).
+    const int parts = P * P >= NT ? 1 : NT / (P * P);
+    for (int i = threadIdx.x; i < P * P * parts; i += NT) {
+        const int pc = i / (P * P), pq = i % (P * P), pg = pq / P, g = pq % P;
+        int sum = 0;
+        int s = g * epg + pc;
+        for (; s + 3 * parts < (g + 1) * epg; s += 4 * parts) {
+            int c[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int b = (s + q * parts) * P + pg;
+                c[q] = s_start[b + 1] - s_start[b];
+            }
+            sum += (c[0] + c[1]) + (c[2] + c[3]);
+        }
+        for (; s < (g + 1) * epg; s += parts) sum += s_start[s * P + pg + 1] - s_start[s * P + pg];
+        atomicAdd(&s_pair[pq], sum);
     }
+    __syncthreads();
+    for (int i = threadIdx.x; i < P * P; i += NT) p.o.pair_count[i] = s_pair[i];
 }
 
 // Empty layers only (no scatter runs): the offsets of zero assignments.
@@ -152,8 +213,9 @@ __global__ __launch_bounds__(1024) void k_scan(ShParams p)
     __shared__ int smem[17];
     __shared__ int s_start[kMaxBuckets + 1];
     __shared__ int s_tstart[65];
+    __shared__ int s_pair[64 * 64];
     bucket_starts<1024>(p, smem, s_start, s_tstart);
-    write_offsets<1024>(p, s_start, s_tstart);
+    write_offsets<1024>(p, s_start, s_tstart, s_pair);
 }
 
 __global__ __launch_bounds__(kThreads) void k_scatter(ShParams p)
@@ -174,31 +236,64 @@ __global__ __launch_bounds__(kThreads) void k_scatter(ShParams p)
     __shared__ int s_smem[17];
     __shared__ int s_start[kMaxBuckets + 1];
     __shared__ int s_tstart[65];
+    __shared__ int s_gp[kMaxTPB];   // predicted group of each of the block's tokens
     bucket_starts<kThreads>(p, s_smem, s_start, s_tstart);
-    if (b == 0) write_offsets<kThreads>(p, s_start, s_tstart);
-    for (int i = threadIdx.x; i < 4 * nbk; i += kThreads) base[i / nbk][i % nbk] = 0;
-    for (int i = threadIdx.x; i < 4 * 64; i += kThreads) tbase[i / 64][i % 64] = 0;
+    if (b == 0) {
+        write_offsets<kThreads>(p, s_start, s_tstart, &base[0][0]);
+        __syncthreads();   // its pair scratch (base) is zeroed below
+    }
+    for (int i = threadIdx.x; i < nbk; i += kThreads) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) base[q][i] = 0;
+    }
+    if (threadIdx.x < 64) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) tbase[q][threadIdx.x] = 0;
+    }
     for (int i = threadIdx.x; i <= nt; i += kThreads) s_rp[i] = p.row_ptr[t0 + i];
+    for (int i = threadIdx.x; i < nt; i += kThreads) s_gp[i] = p.o.g_pred[t0 + i];
     __syncthreads();
     // per-wave counts
     for (int t = tw0 + l; t < tw1; t += 64) {
-        const int g = p.o.g_pred[t];
+        const int g = s_gp[t - t0];
         atomicAdd(&tbase[w][g], 1);
-        for (int a = s_rp[t - t0]; a < s_rp[t - t0 + 1]; ++a)
-            atomicAdd(&base[w][clampi(p.slot[a], 0, p.E - 1) * P + g], 1);
+        const int a1 = s_rp[t - t0 + 1];
+        for (int a = s_rp[t - t0]; a < a1; a += 8) {
+            int s[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) s[q] = a + q < a1 ? p.slot[a + q] : -1;
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                if (a + q < a1) atomicAdd(&base[w][clampi(s[q], 0, p.E - 1) * P + g], 1);
+        }
     }
     __syncthreads();
     // counts -> starting positions: block offset + earlier waves' counts
-    for (int i = threadIdx.x; i < nbk; i += kThreads) {
-        int run = s_start[i] + p.o.hist[(size_t)i * p.nb + b];
-        for (int q = 0; q < 4; ++q) {
-            const int c = base[q][i];
-            base[q][i] = run;
-            run += c;
+    {
+        // this block's row of the offset table, loaded before it is used
+        constexpr int kPerB = (kMaxBuckets + kThreads - 1) / kThreads;
+        int hv[kPerB];
+#pragma unroll
+        for (int q = 0; q < kPerB; ++q) {
+            const int i = threadIdx.x + q * kThreads;
+            hv[q] = i < nbk ? p.o.hist[(size_t)b * nbk + i] : 0;
+        }
+#pragma unroll
+        for (int q = 0; q < kPerB; ++q) {
+            const int i = threadIdx.x + q * kThreads;
+            if (i < nbk) {
+                int run = s_start[i] + hv[q];
+#pragma unroll
+                for (int wq = 0; wq < 4; ++wq) {
+                    const int c = base[wq][i];
+                    base[wq][i] = run;
+                    run += c;
+                }
+            }
         }
     }
     if (threadIdx.x < P) {
-        int run = s_tstart[threadIdx.x] + p.o.thist[threadIdx.x * p.nb + b];
+        int run = s_tstart[threadIdx.x] + p.o.thist[(size_t)b * P + threadIdx.x];
         for (int q = 0; q < 4; ++q) {
             const int c = tbase[q][threadIdx.x];
             tbase[q][threadIdx.x] = run;
@@ -209,9 +304,12 @@ __global__ __launch_bounds__(kThreads) void k_scatter(ShParams p)
 
     // assignments of this wave's tokens, 64 at a time, in assignment order
     const int a_begin = s_rp[tw0 - t0], a_end = s_rp[tw1 - t0];
+    int nslot = a_begin + l < a_end ? p.slot[a_begin + l] : 0;   // next chunk's slot, loaded ahead
     for (int c0 = a_begin; c0 < a_end; c0 += 64) {
         const int a = c0 + l;
         const bool valid = a < a_end;
+        const int myslot = nslot;
+        if (c0 + 64 + l < a_end) nslot = p.slot[c0 + 64 + l];
         uint32_t bucket = 0;
         int t = 0;
         if (valid) {
@@ -222,7 +320,7 @@ __global__ __launch_bounds__(kThreads) void k_scatter(ShParams p)
                 if (s_rp[mid] <= a) lo = mid; else hi = mid - 1;
             }
             t = t0 + lo;
-            bucket = (uint32_t)(clampi(p.slot[a], 0, p.E - 1) * P + p.o.g_pred[t]);
+            bucket = (uint32_t)(clampi(myslot, 0, p.E - 1) * P + s_gp[lo]);
         }
         const uint64_t act = __ballot(valid);
         const uint64_t peers = match_key(bucket, p.bucket_bits, act);
@@ -240,7 +338,7 @@ __global__ __launch_bounds__(kThreads) void k_scatter(ShParams p)
     for (int c0 = tw0; c0 < tw1; c0 += 64) {
         const int t = c0 + l;
         const bool valid = t < tw1;
-        const uint32_t g = valid ? (uint32_t)p.o.g_pred[t] : 0u;
+        const uint32_t g = valid ? (uint32_t)s_gp[t - t0] : 0u;
         const uint64_t act = __ballot(valid);
         const uint64_t peers = match_key(g, p.group_bits, act);
         if (valid) {
@@ -253,29 +351,34 @@ __global__ __launch_bounds__(kThreads) void k_scatter(ShParams p)
 
 // x_sorted[assign_to_sorted[a]] = x[t] for every assignment a of token t:
 // each x row is read once and written k_t times.  One wave per token, 16-byte
-// chunks.
+// chunks.  The token's k_t destinations are read once, one per lane, and
+// handed to the stores with readlane (an index load between two stores would
+// wait for the earlier store: vector memory counters retire in order).
 __global__ __launch_bounds__(kThreads) void k_gather(int T, int row_bytes,
                                                      const char* __restrict__ x,
                                                      const int32_t* __restrict__ row_ptr,
                                                      const int32_t* __restrict__ a2s,
                                                      char* __restrict__ xs)
 {
-    const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
     const int l = threadIdx.x & 63;
     if (t >= T) return;
     const int nch = row_bytes >> 4;
     const int a0 = row_ptr[t], a1 = row_ptr[t + 1];
+    const int kt = a1 - a0;
+    const int my_s = l < kt ? a2s[a0 + l] : 0;
     const u32x4_t* src = (const u32x4_t*)(x + (size_t)t * row_bytes);
     for (int c = l; c < nch; c += 4 * 64) {
         u32x4_t v[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q)
             if (c + q * 64 < nch) v[q] = src[c + q * 64];
-        for (int a = a0; a < a1; ++a) {
-            u32x4_t* dst = (u32x4_t*)(xs + (size_t)a2s[a] * row_bytes);
+        for (int j = 0; j < kt; ++j) {
+            const int s = __builtin_amdgcn_readlane(my_s, j);
+            u32x4_t* dst = (u32x4_t*)(xs + (size_t)s * row_bytes);
 #pragma unroll
             for (int q = 0; q < 4; ++q)
-                if (c + q * 64 < nch) dst[c + q * 64] = v[q];
+                if (c + q * 64 < nch) __builtin_nontemporal_store(v[q], &dst[c + q * 64]);
         }
     }
 }
@@ -323,7 +426,7 @@ hipError_t launch_shuffle(const moe_cfg& c, int nb, int tpb, const int32_t* row_
     p.o = o;
     // the histogram kernel also runs for T == 0 so the table it writes is zero
     hipLaunchKernelGGL(k_hist, dim3(nb), dim3(kThreads), 0, s, p);
-    hipLaunchKernelGGL(k_rowscan, dim3(ceil_div(p.nbk + c.P, 4)), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(k_rowscan, dim3(ceil_div(p.nbk + c.P, 64)), dim3(kThreads), 0, s, p);
     if (c.T > 0)
         hipLaunchKernelGGL(k_scatter, dim3(nb), dim3(kThreads), 0, s, p);
     else
