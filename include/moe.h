@@ -84,6 +84,19 @@ enum moe_stage {
     MOE_NSTAGES = 6
 };
 
+/* Bits of the device data-error word that libraries built with device data
+ * checks (libmoe_debug.so) set when a kernel meets an out-of-range input
+ * value.  Every library clamps such values (or skips the entry) so that no
+ * access leaves its buffer; only the debug build records them. */
+enum moe_data_error {
+    MOE_DATA_TOKEN_ID = 1,   /* tok[t] outside [0, V) */
+    MOE_DATA_LUT = 2,        /* lut[v] outside [0, P) */
+    MOE_DATA_SLOT = 4,       /* topk_slot[a] outside [0, E) */
+    MOE_DATA_K = 8,          /* k_tok[t] outside [0, k_max] */
+    MOE_DATA_PLACEMENT = 16, /* slot_to_orig[s] outside [0, E) */
+    MOE_DATA_PREF = 32       /* pref entry outside [0, E) (skipped) */
+};
+
 /* Layer description (host struct). */
 typedef struct moe_cfg {
     int32_t T;            /* tokens */
@@ -142,6 +155,23 @@ size_t moe_route_workspace_bytes(const moe_cfg* cfg);
 /* Text of the last error on the calling thread (never NULL). */
 const char* moe_last_error(void);
 
+/* 1 when this library was built with device data checks (libmoe_debug.so),
+ * 0 for the release build.  Host only. */
+int32_t moe_debug_checks(void);
+
+/*
+ * Device data errors (debug builds only; not on the hot path): reads into *flags (host) the moe_data_error bits recorded in
+ * the error word at the start of workspace ws -- every workspace that
+ * moe_workspace_bytes or moe_route_workspace_bytes sizes begins with it -- or,
+ * with ws == NULL, in the static scratch of moe_shuffle_noalloc on the
+ * current device; clear != 0 zeroes the word afterwards.  The word
+ * accumulates until cleared: a fresh workspace must be cleared once before
+ * its first call (or its initial contents read as errors).  SYNCHRONOUS:
+ * waits on `stream`.  The release build returns MOE_EINVAL (it records
+ * nothing).  MOE_EINVAL also for flags == NULL.
+ */
+int32_t moe_debug_errors(const void* ws, uint32_t* flags, int32_t clear, void* stream);
+
 /*
  * Route: gate GEMM (MFMA), affinity bias, top-k selection and weights.
  * Passages: each token activates the few experts its gate picks, which is
@@ -175,8 +205,9 @@ const char* moe_last_error(void);
  * Workspace: moe_route_workspace_bytes(cfg) bytes (device, 256-byte
  * aligned), or NULL when that is 0.  bf16 layers with E > 64 run the gate
  * GEMM as its own tiled kernel and keep its fp32 partial logits there; every
- * other layer computes the gate inside the route kernel.  MOE_EWORKSPACE if
- * it is missing or too small.
+ * other layer computes the gate inside the route kernel.  In debug builds the
+ * workspace also holds the data-error word, so it is never 0 there.
+ * MOE_EWORKSPACE if it is missing or too small.
  */
 int32_t moe_route(const moe_cfg* cfg, const void* x, const void* Wg, const float* ebias,
                   const int32_t* slot_to_orig, const int32_t* tok, const int32_t* pref,

@@ -33,7 +33,8 @@ def test_header_declares_the_boundary():
         "moe_route_workspace_bytes",
         "moe_token_group_counts", "moe_lut_from_counts", "moe_expert_group_counts",
         "moe_balanced_assign", "moe_optimize_placement", "moe_request_group_hist",
-        "moe_sigmoid", "moe_pack_weights", "moe_shuffle_noalloc"])
+        "moe_sigmoid", "moe_pack_weights", "moe_shuffle_noalloc", "moe_debug_checks",
+        "moe_debug_errors"])
 
 
 def test_library_exports_every_declared_symbol(m):
@@ -314,3 +315,24 @@ def test_coscheduling_calls_reject_bad_arguments(m):
                                     group.ctypes.data_as(ctypes.c_void_p), None, fake, fake, fake,
                                     None, None, None)
     assert rc == m.MOE_EINVAL
+
+
+def test_debug_library_exports_every_declared_symbol_and_reports_its_build(m):
+    """libmoe_debug.so (device data checks) has the same ABI; only it records
+    data errors, and its route workspace always holds the error word."""
+    from token_routing_shuffle_amd import workload as wl
+    with m.use_library(m.DEBUG_LIB_PATH) as dbg:
+        for name in declared_functions():
+            assert hasattr(dbg, name), name
+        assert m.moe_debug_checks() == 1
+        for name, cfg in wl.CONFIGS.items():
+            c = m.make_cfg(cfg)
+            assert m.moe_route_workspace_bytes(c) >= 256, name
+            assert m.moe_workspace_bytes(c) == m.lib().moe_workspace_bytes(ctypes.byref(c))
+        assert dbg.moe_debug_errors(None, None, 0, None) == m.MOE_EINVAL
+    assert m.moe_debug_checks() == 0
+    flags = ctypes.c_uint32(7)
+    assert m.lib().moe_debug_errors(None, ctypes.byref(flags), 0, None) == m.MOE_EINVAL
+    assert flags.value == 0
+    assert "release build" in m.moe_last_error()
+    assert m.lib().moe_debug_errors(None, None, 0, None) == m.MOE_EINVAL

@@ -1,4 +1,5 @@
-"""Build libmoe.so (HIP, gfx950) in-tree with hipcc.
+"""Build libmoe.so (HIP, gfx950) and its device-data-check variant
+libmoe_debug.so in-tree with hipcc.
 
     python -m token_routing_shuffle_amd.build
 """
@@ -25,12 +26,23 @@ FLAGS = [
 ]
 
 
-def build(verbose=False):
-    os.makedirs(BUILD, exist_ok=True)
+VARIANTS = {
+    # release: the product library
+    "release": (LIB, []),
+    # device data checks: kernels also record clamped input values in the
+    # workspace error word (moe_debug_errors)
+    "debug": (os.path.join(HERE, "libmoe_debug.so"), ["-DMOE_DEBUG_CHECKS=1"]),
+}
+
+
+def build_variant(name, verbose=False):
+    out, defines = VARIANTS[name]
+    bdir = os.path.join(BUILD, name)
+    os.makedirs(bdir, exist_ok=True)
 
     def compile_one(src):
-        obj = os.path.join(BUILD, src + ".o")
-        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+        obj = os.path.join(bdir, src + ".o")
+        cmd = [HIPCC, *FLAGS, *defines, "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError("hipcc failed for %s:\n%s" % (src, r.stderr))
@@ -40,13 +52,20 @@ def build(verbose=False):
 
     with ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose=False):
+    """Both libraries; returns the release library's path."""
+    with ThreadPoolExecutor(max_workers=2) as ex:
+        paths = list(ex.map(lambda n: build_variant(n, verbose), ["release", "debug"]))
+    return paths[0]
 
 
 if __name__ == "__main__":

@@ -113,6 +113,7 @@ WsLayout ws_layout(const moe_cfg& c)
     const size_t Ish = (size_t)c.n_shared * c.I_shared;
     L.tpb = shuffle_tpb(c.T, c.E, c.P);
     L.nb = std::max(1, ceil_div(c.T, L.tpb));
+    L.err = take(4);
     L.row_ptr = take((T + 1) * 4);
     L.topk_slot = take(A * 4);
     L.topk_w = take(A * 4);
@@ -144,7 +145,7 @@ WsLayout ws_layout(const moe_cfg& c)
     // The tiled gate GEMM's partial logits live at the start of the expert
     // FFN buffers: the route is done before the FFN writes them.
     L.glog = L.h;
-    L.route_need = 0;
+    L.route_need = MOE_DEBUG_CHECKS ? L.err + 256 : 0;
     if (gate_tiled(c) && c.T > 0) {
         L.route_need = L.glog + (((size_t)gate_split(c) * T * E * 4 + 255) & ~(size_t)255);
         L.total = std::max(L.total, L.route_need);
@@ -167,6 +168,13 @@ using namespace moe;
     do {                                                                        \
         if (!aligned16(ptr)) return fail(MOE_EINVAL, "%s not 16-byte aligned", #ptr); \
     } while (0)
+
+// The data-error word of a workspace (debug builds), else nullptr.
+static uint32_t* err_word(void* ws, const WsLayout& L)
+{
+    if (!MOE_DEBUG_CHECKS || ws == nullptr) return nullptr;
+    return (uint32_t*)((char*)ws + L.err);
+}
 
 static int32_t check_ws(const void* ws, size_t ws_bytes, size_t need)
 {
@@ -193,6 +201,26 @@ MOE_API size_t moe_workspace_bytes(const moe_cfg* cfg)
 
 MOE_API const char* moe_last_error(void) { return g_err; }
 
+MOE_API int32_t moe_debug_checks(void) { return MOE_DEBUG_CHECKS ? 1 : 0; }
+
+MOE_API int32_t moe_debug_errors(const void* ws, uint32_t* flags, int32_t clear, void* stream)
+{
+    REQUIRE(flags);
+    *flags = 0;
+    if (!MOE_DEBUG_CHECKS) return fail(MOE_EINVAL, "release build: no device data checks recorded");
+    void* word = const_cast<void*>(ws);
+    hipError_t e = hipSuccess;
+    if (word == nullptr) {
+        e = noalloc_scratch(&word);   // the error word starts the static scratch
+        if (e != hipSuccess) return hip_fail(e, "moe_debug_errors");
+    }
+    hipStream_t s = (hipStream_t)stream;
+    e = hipMemcpyAsync(flags, word, sizeof(uint32_t), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess && clear) e = hipMemsetAsync(word, 0, sizeof(uint32_t), s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_debug_errors");
+}
+
 MOE_API size_t moe_route_workspace_bytes(const moe_cfg* cfg)
 {
     if (check_cfg(cfg) != MOE_OK) return 0;
@@ -212,8 +240,9 @@ MOE_API int32_t moe_route(const moe_cfg* cfg, const void* x, const void* Wg, con
     if (L.route_need > 0) {
         rc = check_ws(ws, ws_bytes, L.route_need);
         if (rc != MOE_OK) return rc;
-        glog = at<float>(ws, L.glog);
+        if (gate_tiled(c) && c.T > 0) glog = at<float>(ws, L.glog);
     }
+    uint32_t* err = L.route_need > 0 ? err_word(ws, L) : nullptr;
     REQUIRE(row_ptr);
     if (c.T > 0) {
         REQUIRE(x);
@@ -227,10 +256,10 @@ MOE_API int32_t moe_route(const moe_cfg* cfg, const void* x, const void* Wg, con
         if (c.ragged) REQUIRE(k_tok);
     }
     hipStream_t s = (hipStream_t)stream;
-    hipError_t e = launch_row_ptr(c, k_tok, row_ptr, s);
+    hipError_t e = launch_row_ptr(c, k_tok, row_ptr, err, s);
     if (e == hipSuccess)
         e = launch_route(c, x, Wg, ebias, slot_to_orig, tok, pref, k_tok, row_ptr, topk_slot, topk_w,
-                         logits, glog, s);
+                         logits, glog, err, s);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_route");
 }
 
@@ -310,16 +339,18 @@ MOE_API int32_t moe_shuffle(const moe_cfg* cfg, const int32_t* row_ptr, const in
     o.rowtot = at<int32_t>(ws, L.rowtot);
     o.bstart = at<int32_t>(ws, L.bstart);
     o.tstart = at<int32_t>(ws, L.tstart);
+    o.err = err_word(ws, L);
     hipStream_t s = (hipStream_t)stream;
     hipError_t e = launch_shuffle(c, L.nb, L.tpb, row_ptr, topk_slot, tok, lut, o, s);
     if (e == hipSuccess && x_sorted != nullptr) e = launch_gather(c, x, row_ptr, assign_to_sorted, x_sorted, s);
     return e == hipSuccess ? MOE_OK : hip_fail(e, "moe_shuffle");
 }
 
-// Scratch of the shuffle alone, packed from offset 0: g_pred [T], the
-// per-block histograms hist [E*P][nb] and thist [P][nb], row totals, bucket
-// and group starts (256-byte aligned sections).  Returns the bytes needed.
-static size_t shuffle_scratch(const moe_cfg& c, ShuffleOut& o, char* base, int* nb, int* tpb)
+// Scratch of the shuffle alone, packed from offset 0: the data-error word,
+// g_pred [T], the per-block histograms hist [nb][E*P] and thist [nb][P], row
+// totals, bucket and group starts (256-byte aligned sections) at `base` (0:
+// sizes only).  Returns the bytes needed.
+static size_t shuffle_scratch(const moe_cfg& c, ShuffleOut& o, uintptr_t base, int* nb, int* tpb)
 {
     *tpb = shuffle_tpb(c.T, c.E, c.P);
     *nb = std::max(1, ceil_div(c.T, *tpb));
@@ -330,6 +361,8 @@ static size_t shuffle_scratch(const moe_cfg& c, ShuffleOut& o, char* base, int* 
         off += (bytes + 255) & ~(size_t)255;
         return p;
     };
+    uint32_t* err = (uint32_t*)take(4);
+    o.err = MOE_DEBUG_CHECKS && base != 0 ? err : nullptr;
     o.g_pred = take((size_t)c.T * 4);
     o.hist = take(E * P * NB * 4);
     o.thist = take(P * NB * 4);
@@ -356,14 +389,14 @@ MOE_API int32_t moe_shuffle_noalloc(const moe_cfg* cfg, const int32_t* row_ptr, 
     ShuffleOut o = shuffle_outputs(expert_count, expert_off, group_count, group_off, pair_count, tok_perm,
                                    tok_off, sorted_to_assign, assign_to_sorted);
     int nb = 0, tpb = 0;
-    const size_t need = shuffle_scratch(c, o, nullptr, &nb, &tpb);
+    const size_t need = shuffle_scratch(c, o, 0, &nb, &tpb);
     if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES)
         return fail(MOE_EWORKSPACE, "moe_shuffle_noalloc: layer needs %zu bytes of scratch, the static "
                     "array holds %zu", need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
     void* base = nullptr;
     hipError_t e = noalloc_scratch(&base);
     if (e != hipSuccess) return hip_fail(e, "moe_shuffle_noalloc (scratch address)");
-    shuffle_scratch(c, o, (char*)base, &nb, &tpb);
+    shuffle_scratch(c, o, (uintptr_t)base, &nb, &tpb);
     hipStream_t s = (hipStream_t)stream;
     e = launch_shuffle(c, nb, tpb, row_ptr, topk_slot, tok, lut, o, s);
     if (e == hipSuccess && x_sorted != nullptr) e = launch_gather(c, x, row_ptr, assign_to_sorted, x_sorted, s);
@@ -746,6 +779,7 @@ MOE_API int32_t moe_forward(const moe_cfg* cfg, const moe_weights* w, const moe_
     o.bstart = at<int32_t>(ws, L.bstart);
     o.tstart = at<int32_t>(ws, L.tstart);
     o.gemm_ctr = at<int32_t>(ws, L.gemm_ctr);   // zeroed by the shuffle for the FFN below
+    o.err = err_word(ws, L);
     void* x_sorted = c.fuse_gather ? nullptr : (X->x_sorted ? X->x_sorted : at<void>(ws, L.x_sorted));
     void* y_sorted = X->y_sorted ? X->y_sorted : at<void>(ws, L.y_sorted);
     void* y_sh = c.n_shared > 0 ? (X->y_shared ? X->y_shared : at<void>(ws, L.y_sh)) : nullptr;
@@ -760,10 +794,10 @@ MOE_API int32_t moe_forward(const moe_cfg* cfg, const moe_weights* w, const moe_
         if (e == hipSuccess) e = (expr);    \
     } while (0)
     STEP(record(X, MOE_STAGE_ROUTE, 0, s));
-    STEP(launch_row_ptr(c, in->k_tok, row_ptr, s));
+    STEP(launch_row_ptr(c, in->k_tok, row_ptr, o.err, s));
     STEP(launch_route(c, in->x, w->Wg, w->ebias, w->slot_to_orig, in->tok, w->pref, in->k_tok,
                       row_ptr, topk_slot, topk_w, X->logits,
-                      L.route_need > 0 ? at<float>(ws, L.glog) : nullptr, s));
+                      gate_tiled(c) && c.T > 0 ? at<float>(ws, L.glog) : nullptr, o.err, s));
     STEP(record(X, MOE_STAGE_ROUTE, 1, s));
     STEP(record(X, MOE_STAGE_SHUFFLE, 0, s));
     STEP(launch_shuffle(c, L.nb, L.tpb, row_ptr, topk_slot, in->tok, w->lut, o, s));

@@ -165,6 +165,31 @@ MOE_DEV void lds_barrier()
 
 MOE_DEV int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
+// Device data checks.  Kernels clamp input values they index with (token
+// ids, table entries, slots, budgets) so that bad data cannot send a load out
+// of bounds.  A library built with MOE_DEBUG_CHECKS=1 also records every
+// clamp or skip in a workspace error word (bits moe_data_error of moe.h);
+// the release build compiles the check away.
+#ifndef MOE_DEBUG_CHECKS
+#define MOE_DEBUG_CHECKS 0
+#endif
+
+MOE_DEV void data_error(uint32_t* err, uint32_t bit)
+{
+    if constexpr (MOE_DEBUG_CHECKS) {
+        if (err != nullptr) atomicOr(err, bit);
+    } else {
+        (void)err;
+        (void)bit;
+    }
+}
+
+MOE_DEV int checked_clamp(int v, int lo, int hi, uint32_t* err, uint32_t bit)
+{
+    if (v < lo || v > hi) data_error(err, bit);
+    return clampi(v, lo, hi);
+}
+
 // Own fp32 exp: Cody-Waite additive range reduction n = rint(x*log2 e),
 // r = x - n*ln2 with ln2 split into an fp32 high part and the fp32 rounding
 // of the remainder (one fused multiply-add each), exp(r) by the degree-7

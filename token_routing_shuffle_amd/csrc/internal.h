@@ -7,6 +7,10 @@
 
 #include "../../include/moe.h"
 
+#ifndef MOE_DEBUG_CHECKS
+#define MOE_DEBUG_CHECKS 0   // 1: kernels record clamped input data (libmoe_debug.so)
+#endif
+
 namespace moe {
 
 // Tokens per block of the histogram / scatter kernels of the shuffle: 256,
@@ -28,6 +32,7 @@ inline int ilog2(int v) { int r = 0; while ((1 << r) < v) ++r; return r; }
 
 // Workspace layout (byte offsets, 256-byte aligned sections).
 struct WsLayout {
+    size_t err;                                   // data-error word (first 256 bytes)
     size_t row_ptr, topk_slot, topk_w;            // route outputs (moe_forward)
     size_t g_pred, hist, thist, rowtot, bstart, tstart;  // shuffle scratch
     size_t expert_count, expert_off, group_count, group_off, pair_count;
@@ -47,12 +52,13 @@ bool gate_tiled(const moe_cfg& c);
 int gate_split(const moe_cfg& c);
 
 // --- launchers (no argument checks; callers validate) ---------------------
-hipError_t launch_row_ptr(const moe_cfg& c, const int32_t* k_tok, int32_t* row_ptr,
+// err: the data-error word (debug builds; nullptr in the release build)
+hipError_t launch_row_ptr(const moe_cfg& c, const int32_t* k_tok, int32_t* row_ptr, uint32_t* err,
                           hipStream_t s);
 hipError_t launch_route(const moe_cfg& c, const void* x, const void* Wg, const float* ebias,
                         const int32_t* slot_to_orig, const int32_t* tok, const int32_t* pref,
                         const int32_t* k_tok, int32_t* row_ptr, int32_t* topk_slot,
-                        float* topk_w, float* logits, float* glog, hipStream_t s);
+                        float* topk_w, float* logits, float* glog, uint32_t* err, hipStream_t s);
 
 struct ShuffleOut {
     int32_t *expert_count, *expert_off, *group_count, *group_off, *pair_count;
@@ -60,6 +66,7 @@ struct ShuffleOut {
     int32_t *g_pred, *hist, *thist;
     int32_t *rowtot, *bstart, *tstart;  // row totals, bucket and group starts (scratch)
     int32_t* gemm_ctr;  // [16] grouped-GEMM tile counters to zero, or nullptr
+    uint32_t* err;      // data-error word (debug builds), or nullptr
 };
 hipError_t launch_sigmoid(const float* x, float* y, int64_t n, hipStream_t s);
 

@@ -36,13 +36,14 @@ struct RouteParams {
     float* logits;
     const float* glog;  // [gS][T][E] partial logits of the tiled gate GEMM, or nullptr
     int gS;
+    uint32_t* err;      // data-error word (debug builds), or nullptr
 };
 
 // CSR offsets: row_ptr[t] = sum of k over tokens < t (k_tok clamped to
 // [0, k_max] so that A never exceeds T*k_max).
 __global__ __launch_bounds__(1024) void k_row_ptr(int T, int k_max, int ragged,
                                                    const int32_t* __restrict__ k_tok,
-                                                   int32_t* __restrict__ row_ptr)
+                                                   int32_t* __restrict__ row_ptr, uint32_t* err)
 {
     __shared__ int smem[17];
     if (!ragged) {
@@ -56,7 +57,7 @@ __global__ __launch_bounds__(1024) void k_row_ptr(int T, int k_max, int ragged,
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int t = base + threadIdx.x * 4 + q;
-            v[q] = t < T ? clampi(k_tok[t], 0, k_max) : 0;
+            v[q] = t < T ? checked_clamp(k_tok[t], 0, k_max, err, MOE_DATA_K) : 0;
             sum += v[q];
         }
         int total;
@@ -195,7 +196,12 @@ __global__ __launch_bounds__(kThreads) void k_route(RouteParams p)
     const int T = p.T, H = p.H, E = p.E;
 
     __shared__ int s_rp[kBM], s_kt[kBM];
-    for (int s = tid; s < EP; s += kThreads) s_s2o[s] = s < E ? clampi(p.s2o[s], 0, E - 1) : s;
+    // s_o2s starts at slot 0 everywhere, so that a slot_to_orig that is not
+    // a permutation (clamped entries, duplicates) leaves no entry unset
+    for (int s = tid; s < EP; s += kThreads) {
+        s_s2o[s] = s < E ? checked_clamp(p.s2o[s], 0, E - 1, p.err, MOE_DATA_PLACEMENT) : s;
+        s_o2s[s] = 0;
+    }
     if (tid < kBM) {
         const int t = t0 + tid;
         if (p.ragged) {
@@ -205,22 +211,22 @@ __global__ __launch_bounds__(kThreads) void k_route(RouteParams p)
             if (t < T) p.row_ptr[t] = t * p.k_max;
             if (t == T - 1) p.row_ptr[T] = T * p.k_max;
         }
-        s_kt[tid] = t >= T ? 0 : (p.ragged ? clampi(p.k_tok[t], 0, p.k_max) : p.k_max);
+        s_kt[tid] = t >= T ? 0 : (p.ragged ? checked_clamp(p.k_tok[t], 0, p.k_max, p.err, MOE_DATA_K) : p.k_max);
     }
     // the affinity table is read before the GEMM so its latency overlaps it
     const bool do_bias = p.pref != nullptr && p.aff_bias != 0.0f && p.n_pref > 0;
     const int np = p.n_pref;
-    int pre_o[4], pre_row[4];
+    int pre_o[4], pre_row[4];   // pre_row -1: no entry
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-        pre_o[q] = -1;
-        pre_row[q] = 0;
+        pre_o[q] = 0;
+        pre_row[q] = -1;
         const int idx = tid + q * kThreads;
         if (do_bias && idx < kBM * np) {
             const int row = idx / np, j = idx % np;
             const int t = t0 + row;
             if (t < T) {
-                const int v = clampi(p.tok[t], 0, p.V - 1);
+                const int v = checked_clamp(p.tok[t], 0, p.V - 1, p.err, MOE_DATA_TOKEN_ID);
                 pre_o[q] = p.pref[(size_t)v * np + j];
                 pre_row[q] = row;
             }
@@ -332,15 +338,20 @@ __global__ __launch_bounds__(kThreads) void k_route(RouteParams p)
     // ---------------- synthetic affinity bias ----------------
     if (do_bias) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q)
-            if (pre_o[q] >= 0 && pre_o[q] < E) s_log[pre_row[q]][s_o2s[pre_o[q]]] += p.aff_bias;
+        for (int q = 0; q < 4; ++q) {
+            if (pre_row[q] >= 0) {
+                if (pre_o[q] >= 0 && pre_o[q] < E) s_log[pre_row[q]][s_o2s[pre_o[q]]] += p.aff_bias;
+                else data_error(p.err, MOE_DATA_PREF);
+            }
+        }
         for (int idx = tid + 4 * kThreads; idx < kBM * np; idx += kThreads) {
             const int row = idx / np, j = idx % np;
             const int t = t0 + row;
             if (t < T) {
-                const int v = clampi(p.tok[t], 0, p.V - 1);
+                const int v = checked_clamp(p.tok[t], 0, p.V - 1, p.err, MOE_DATA_TOKEN_ID);
                 const int o = p.pref[(size_t)v * np + j];
                 if (o >= 0 && o < E) s_log[row][s_o2s[o]] += p.aff_bias;
+                else data_error(p.err, MOE_DATA_PREF);
             }
         }
         __syncthreads();
@@ -539,11 +550,12 @@ hipError_t launch_sigmoid(const float* x, float* y, int64_t n, hipStream_t s)
     return hipGetLastError();
 }
 
-hipError_t launch_row_ptr(const moe_cfg& c, const int32_t* k_tok, int32_t* row_ptr, hipStream_t s)
+hipError_t launch_row_ptr(const moe_cfg& c, const int32_t* k_tok, int32_t* row_ptr, uint32_t* err,
+                          hipStream_t s)
 {
     // with a fixed k and T > 0 the route kernel writes row_ptr itself
     if (!c.ragged && c.T > 0) return hipSuccess;
-    hipLaunchKernelGGL(k_row_ptr, dim3(1), dim3(1024), 0, s, c.T, c.k_max, c.ragged, k_tok, row_ptr);
+    hipLaunchKernelGGL(k_row_ptr, dim3(1), dim3(1024), 0, s, c.T, c.k_max, c.ragged, k_tok, row_ptr, err);
     return hipGetLastError();
 }
 
@@ -566,10 +578,11 @@ int gate_split(const moe_cfg& c)
 hipError_t launch_route(const moe_cfg& c, const void* x, const void* Wg, const float* ebias,
                         const int32_t* slot_to_orig, const int32_t* tok, const int32_t* pref,
                         const int32_t* k_tok, int32_t* row_ptr, int32_t* topk_slot,
-                        float* topk_w, float* logits, float* glog, hipStream_t s)
+                        float* topk_w, float* logits, float* glog, uint32_t* err, hipStream_t s)
 {
     if (c.T == 0) return hipSuccess;
     RouteParams p;
+    p.err = err;
     p.T = c.T;
     p.H = c.H;
     p.E = c.E;

@@ -51,8 +51,8 @@ __global__ __launch_bounds__(kThreads) void k_hist(ShParams p)
     if (threadIdx.x < 64) tcnt[threadIdx.x] = 0;
     __syncthreads();
     for (int t = t0 + threadIdx.x; t < t1; t += kThreads) {
-        const int v = clampi(p.tok[t], 0, p.V - 1);
-        const int g = clampi(p.lut[v], 0, p.P - 1);
+        const int v = checked_clamp(p.tok[t], 0, p.V - 1, p.o.err, MOE_DATA_TOKEN_ID);
+        const int g = checked_clamp(p.lut[v], 0, p.P - 1, p.o.err, MOE_DATA_LUT);
         p.o.g_pred[t] = g;
         atomicAdd(&tcnt[g], 1);
         const int a0 = p.row_ptr[t], a1 = p.row_ptr[t + 1];
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kThreads) void k_hist(ShParams p)
             for (int q = 0; q < 8; ++q) s[q] = a + q < a1 ? p.slot[a + q] : -1;
 #pragma unroll
             for (int q = 0; q < 8; ++q)
-                if (a + q < a1) atomicAdd(&cnt[clampi(s[q], 0, p.E - 1) * p.P + g], 1);
+                if (a + q < a1) atomicAdd(&cnt[checked_clamp(s[q], 0, p.E - 1, p.o.err, MOE_DATA_SLOT) * p.P + g], 1);
         }
     }
     __syncthreads();

@@ -7,6 +7,7 @@ be loaded, importing the library raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from typing import Optional
@@ -15,11 +16,14 @@ import torch  # noqa: F401  (loads the HIP runtime libmoe then binds to)
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
+# the same library built with device data checks (moe_debug_errors)
+DEBUG_LIB_PATH = os.path.join(_HERE, "libmoe_debug.so")
 
 MOE_OK, MOE_EINVAL, MOE_ESHAPE, MOE_EDTYPE, MOE_EWORKSPACE, MOE_EHIP = 0, -1, -2, -3, -4, -5
 MOE_F32, MOE_BF16 = 0, 1
 MOE_GATE_SOFTMAX, MOE_GATE_SIGMOID_GROUPED = 0, 1
 MOE_FFN_ROUTED, MOE_FFN_SHARED = 0, 1
+MOE_DATA_TOKEN_ID, MOE_DATA_LUT, MOE_DATA_SLOT, MOE_DATA_K, MOE_DATA_PLACEMENT, MOE_DATA_PREF = 1, 2, 4, 8, 16, 32
 STAGES = ("route", "shuffle", "gather", "ffn_up", "ffn_down", "combine")
 MOE_NSTAGES = len(STAGES)
 
@@ -60,11 +64,11 @@ class moe_exports(ctypes.Structure):
                                    "x_sorted", "y_sorted", "y_shared", "events")]
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
-        raise OSError("libmoe.so is not built (%s); run: python -m token_routing_shuffle_amd.build"
-                      % LIB_PATH)
-    lib = ctypes.CDLL(LIB_PATH)
+def _load(path=None):
+    path = LIB_PATH if path is None else path
+    if not os.path.exists(path):
+        raise OSError("%s is not built; run: python -m token_routing_shuffle_amd.build" % path)
+    lib = ctypes.CDLL(path)
     # libmoe must bind to the HIP runtime torch already loaded (same SONAME);
     # two runtimes in one process would not share streams or allocations.
     with open("/proc/self/maps") as f:
@@ -81,6 +85,10 @@ def _load():
     lib.moe_route_workspace_bytes.argtypes = [P(moe_cfg)]
     lib.moe_last_error.restype = ctypes.c_char_p
     lib.moe_last_error.argtypes = []
+    lib.moe_debug_checks.restype = i32
+    lib.moe_debug_checks.argtypes = []
+    lib.moe_debug_errors.restype = i32
+    lib.moe_debug_errors.argtypes = [vp, vp, i32, vp]
     lib.moe_route.restype = i32
     lib.moe_route.argtypes = [P(moe_cfg)] + [vp] * 11 + [vp, sz, vp]
     lib.moe_shuffle.restype = i32
@@ -119,6 +127,7 @@ def _load():
 
 
 _lib = None
+_variants = {}
 
 
 def lib():
@@ -128,12 +137,27 @@ def lib():
     return _lib
 
 
+@contextlib.contextmanager
+def use_library(path):
+    """Route every wrapper below to another build of the library (e.g. the
+    device-data-check build at DEBUG_LIB_PATH) inside the block."""
+    global _lib
+    if path not in _variants:
+        _variants[path] = _load(path)
+    prev = lib()
+    _lib = _variants[path]
+    try:
+        yield _lib
+    finally:
+        _lib = prev
+
+
 EXPORTED = ("moe_validate", "moe_workspace_bytes", "moe_route_workspace_bytes", "moe_last_error",
             "moe_route", "moe_shuffle", "moe_shuffle_noalloc",
             "moe_expert_ffn", "moe_combine", "moe_forward", "moe_srs", "moe_sag",
             "moe_token_group_counts", "moe_lut_from_counts", "moe_expert_group_counts",
             "moe_balanced_assign", "moe_optimize_placement", "moe_request_group_hist",
-            "moe_sigmoid", "moe_pack_weights")
+            "moe_sigmoid", "moe_pack_weights", "moe_debug_checks", "moe_debug_errors")
 
 
 def _p(t) -> Optional[int]:
@@ -193,16 +217,38 @@ def moe_route_workspace_bytes(cfg: moe_cfg) -> int:
 
 
 def route_workspace(cfg: moe_cfg, device="cuda"):
-    """Device workspace for moe_route alone (None when the layer needs none)."""
+    """Device workspace for moe_route alone (None when the layer needs none);
+    its data-error word (first bytes) is cleared."""
     n = moe_route_workspace_bytes(cfg)
-    return None if n == 0 else torch.empty(n, dtype=torch.uint8, device=device)
+    if n == 0:
+        return None
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    ws[:256].zero_()
+    return ws
 
 
 def workspace(cfg: moe_cfg, device="cuda"):
+    """Device workspace for every call of this layer; its data-error word
+    (first bytes) is cleared."""
     n = moe_workspace_bytes(cfg)
     if n == 0 and moe_validate(cfg) != MOE_OK:
         raise MoeError(moe_validate(cfg), moe_last_error())
-    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    ws = torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+    ws[:256].zero_()
+    return ws
+
+
+def moe_debug_checks() -> int:
+    return lib().moe_debug_checks()
+
+
+def moe_debug_errors(ws=None, clear=True, stream=None) -> int:
+    """moe_data_error bits recorded in workspace ws (None: the static scratch
+    of moe_shuffle_noalloc); synchronous; debug builds only."""
+    flags = ctypes.c_uint32(0)
+    rc = lib().moe_debug_errors(_p(ws), ctypes.byref(flags), int(bool(clear)), _stream(stream))
+    _check(rc, "moe_debug_errors")
+    return flags.value
 
 
 def _ws(ws):

@@ -105,3 +105,74 @@ def profile_lut(cfg, dev: dict, prof_x: torch.Tensor, prof_tok: np.ndarray,
     rp, sl, tok = profile_routing(cfg, dev, prof_x, prof_tok, chunk)
     group = np.arange(cfg.E, dtype=np.int32) // (cfg.E // cfg.P)
     return lut_of_grouping(cfg, rp, sl, tok, group).cpu().numpy()
+
+
+# ----------------------------------------------------------------------------
+# persisted offline tables
+#
+# Placement, token->group table and the preferred-expert (affinity) table of a
+# layer are offline artefacts (the pages fix placement and the token table
+# before serving, ja technical overview §2.2A and §2.3).  They are saved as one
+# .npz per layer configuration, keyed by a hash of the configuration and of
+# how the token table was profiled, and read back with numpy's non-pickle
+# loader.
+
+TABLE_FORMAT = 1
+
+
+def config_key(cfg, profile_tokens: int, placement: str = "random") -> str:
+    """Hex key of a layer configuration (every LayerConfig field), the
+    profiling-draw size and the placement rule."""
+    import dataclasses
+    import hashlib
+    import json
+    d = dataclasses.asdict(cfg)
+    d["k_choices"] = list(d["k_choices"])
+    blob = json.dumps({"cfg": d, "profile_tokens": int(profile_tokens), "placement": placement,
+                       "format": TABLE_FORMAT}, sort_keys=True)
+    return hashlib.sha256(blob.encode()).hexdigest()[:24]
+
+
+def table_path(directory: str, cfg, profile_tokens: int, placement: str = "random") -> str:
+    import os
+    return os.path.join(directory, "%s_%s.npz" % (cfg.name, config_key(cfg, profile_tokens, placement)))
+
+
+def save_tables(directory: str, cfg, tables, lut, profile_tokens: int, placement: str = "random") -> str:
+    """Write slot_to_orig, perm, lut and (when present) the preferred-expert
+    table and the expert selection bias of a layer; returns the file path."""
+    import os
+    os.makedirs(directory, exist_ok=True)
+    path = table_path(directory, cfg, profile_tokens, placement)
+    arrays = dict(slot_to_orig=np.asarray(tables.slot_to_orig, np.int32),
+                  perm=np.asarray(tables.perm, np.int32), lut=np.asarray(lut, np.int32),
+                  key=np.frombuffer(config_key(cfg, profile_tokens, placement).encode(), np.uint8))
+    if tables.pref is not None:
+        arrays["pref"] = np.asarray(tables.pref, np.int32)
+    if tables.ebias is not None:
+        arrays["ebias"] = np.asarray(tables.ebias, np.float32)
+    tmp = path + ".tmp.npz"
+    np.savez(tmp, **arrays)
+    os.replace(tmp, path)
+    return path
+
+
+def load_tables(directory: str, cfg, profile_tokens: int, placement: str = "random"):
+    """The saved tables of this exact configuration as a dict of arrays, or
+    None when there is no file for it.  A file whose stored key does not
+    match (renamed or corrupted) raises ValueError."""
+    import os
+    path = table_path(directory, cfg, profile_tokens, placement)
+    if not os.path.exists(path):
+        return None
+    with np.load(path, allow_pickle=False) as z:
+        out = {k: z[k] for k in z.files}
+    key = bytes(out.pop("key")).decode()
+    if key != config_key(cfg, profile_tokens, placement):
+        raise ValueError("%s: stored key %s does not match the configuration" % (path, key))
+    E, P, V = cfg.E, cfg.P, cfg.V
+    if out["slot_to_orig"].shape != (E,) or out["perm"].shape != (E,) or out["lut"].shape != (V,):
+        raise ValueError("%s: table shapes do not match the configuration" % path)
+    if not (np.sort(out["slot_to_orig"]) == np.arange(E)).all() or (out["lut"] < 0).any() or (out["lut"] >= P).any():
+        raise ValueError("%s: placement is not a permutation or the token table is out of range" % path)
+    return out
