@@ -32,10 +32,13 @@
  *     layouts; per-expert tensors in slot order.  dtype MOE_BF16: activations
  *     and weights are bf16 (uint16 bit patterns), accumulation fp32;
  *     dtype MOE_F32: everything fp32.
- *   - The caller owns every buffer.  The library allocates no device memory,
- *     keeps no mutable global state and is re-entrant when concurrent calls
- *     use distinct workspaces.  moe_workspace_bytes(cfg) bytes of workspace
- *     (256-byte aligned) are enough for every call.
+ *   - The caller owns every buffer.  The library allocates no device memory
+ *     and is re-entrant when concurrent calls use distinct workspaces.  Its
+ *     only mutable global state: a per-device cache of the compute-unit
+ *     count and of the address of moe_shuffle_noalloc's static scratch (both
+ *     set once, thread-safe), and that scratch itself.
+ *     moe_workspace_bytes(cfg) bytes of workspace (256-byte aligned) are
+ *     enough for every call.
  *   - Calls enqueue kernels on `stream` (a hipStream_t; NULL = the null
  *     stream) and return without synchronising.  Device-side sizes that the
  *     host cannot know (the number of assignments A = row_ptr[T] when k is
