@@ -301,6 +301,45 @@ def test_blocked_weights_bit_identical(key):
     assert torch.equal(a, b)
 
 
+def _packed_reference(W, BN, up, K):
+    """The tile-blocked layout of moe_pack_weights written out with numpy
+    from its definition: per expert, n-tile j and k-step kt the block
+    [BN rows][64 elements]; block row r is operand row j*BN + r (W2), or W1
+    row j*BN/2 + r for r < BN/2 and W3 row j*BN/2 + r - BN/2 after it (W13)."""
+    nexp, rows, _ = W.shape
+    KT, nt, npt = K // 64, rows // BN, BN // 2
+    r = np.arange(BN)
+    out = np.empty((nexp, nt, KT, BN, 64), dtype=W.dtype)
+    for j in range(nt):
+        srow = np.where(r < npt, j * npt + r, rows // 2 + j * npt + (r - npt)) if up else j * BN + r
+        for kt in range(KT):
+            out[:, j, kt] = W[:, srow, kt * 64:(kt + 1) * 64]
+    return out.reshape(W.shape)
+
+
+@pytest.mark.parametrize("key", ["dsv2lite_1000", "prism_1000"])
+def test_pack_weights_layout(key):
+    """moe_pack_weights writes exactly the documented tile-blocked layout
+    (256-wide tiles, and the MoE-Prism shape's 128-wide GEMM1 tiles), checked
+    element by element against a numpy transcription of its definition."""
+    c = case(key)
+    m = moe_mod()
+    cfg = m.make_cfg(c.cfg, weights_blocked=1)
+    W13, W2 = c.dev["W13"], c.dev["W2"]
+    b13, b2 = torch.empty_like(W13), torch.empty_like(W2)
+    m.moe_pack_weights(cfg, m.MOE_FFN_ROUTED, W13, W2, b13, b2)
+    torch.cuda.synchronize()
+    H, I = c.cfg.H, c.cfg.I
+    ish2 = 2 * c.cfg.n_shared * c.cfg.I_shared
+    bn_up = 256 if (2 * I) % 256 == 0 and ish2 % 256 == 0 else 128
+    bn_dn = 256 if H % 256 == 0 else 128
+    ne = min(3, c.cfg.E)   # a few experts (the layout repeats per expert)
+    got13 = b13[:ne].view(torch.int16).cpu().numpy()
+    got2 = b2[:ne].view(torch.int16).cpu().numpy()
+    assert np.array_equal(got13, _packed_reference(W13[:ne].view(torch.int16).cpu().numpy(), bn_up, True, H))
+    assert np.array_equal(got2, _packed_reference(W2[:ne].view(torch.int16).cpu().numpy(), bn_dn, False, I))
+
+
 @pytest.mark.parametrize("name,T", [("dsv2lite", 600), ("tiny", 64), ("prism", 384)])
 def test_relabelling_invariance(name, T):
     """Shuffling gate columns together with the expert weights (a different
