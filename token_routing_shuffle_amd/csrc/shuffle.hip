@@ -77,53 +77,74 @@ __global__ __launch_bounds__(kThreads) void k_hist(ShParams p)
 // exclusive offsets in place, with the column totals.  A block takes 64
 // columns (one per lane: neighbouring lanes read neighbouring columns, so
 // every access to a block row is coalesced) and splits the nb block rows
-// between its four waves: each wave sums its rows, the waves' sums are
+// between its sixteen waves: each wave sums its rows, the waves' sums are
 // scanned through LDS, and each wave rewrites its rows as running offsets.
-__global__ __launch_bounds__(kThreads) void k_rowscan(ShParams p)
+// Up to 256 block rows a wave's rows (at most 16) are read in one batch and
+// kept in registers for the rewrite.
+constexpr int kScanWaves = 16;
+__global__ __launch_bounds__(64 * kScanWaves) void k_rowscan(ShParams p)
 {
-    __shared__ int s_part[4][64];
+    __shared__ int s_part[kScanWaves][64];
     const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
     const int col = blockIdx.x * 64 + l;
     const bool valid = col < p.nbk + p.P;
     const bool bucket = col < p.nbk;
     int32_t* a = bucket ? p.o.hist + col : p.o.thist + (col - p.nbk);
     const size_t stride = bucket ? (size_t)p.nbk : (size_t)p.P;
-    const int per = (p.nb + 3) / 4;
+    const int per = (p.nb + kScanWaves - 1) / kScanWaves;
     const int r0 = min(p.nb, w * per), r1 = min(p.nb, r0 + per);
+    constexpr int kHeld = 16;   // rows a wave keeps in registers between the passes
+    int held[kHeld];
     int sum = 0;
     if (valid) {
-        int r = r0;
-        for (; r + 8 <= r1; r += 8) {
-            int v[8];
+        if (per <= kHeld) {
+            // one batch of loads; the rewrite below reuses the values
 #pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] = a[(size_t)(r + q) * stride];
+            for (int q = 0; q < kHeld; ++q) held[q] = r0 + q < r1 ? a[(size_t)(r0 + q) * stride] : 0;
 #pragma unroll
-            for (int q = 0; q < 8; ++q) sum += v[q];
+            for (int q = 0; q < kHeld; ++q) sum += held[q];
+        } else {
+            int r = r0;
+            for (; r + 8 <= r1; r += 8) {
+                int v[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) v[q] = a[(size_t)(r + q) * stride];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) sum += v[q];
+            }
+            for (; r < r1; ++r) sum += a[(size_t)r * stride];
         }
-        for (; r < r1; ++r) sum += a[(size_t)r * stride];
     }
     s_part[w][l] = sum;
     __syncthreads();
     int run = 0;
     for (int q = 0; q < w; ++q) run += s_part[q][l];
     if (valid) {
-        int r = r0;
-        for (; r + 8 <= r1; r += 8) {
-            int v[8];
+        if (per <= kHeld) {
 #pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] = a[(size_t)(r + q) * stride];
+            for (int q = 0; q < kHeld; ++q) {
+                if (r0 + q < r1) a[(size_t)(r0 + q) * stride] = run;
+                run += held[q];
+            }
+        } else {
+            int r = r0;
+            for (; r + 8 <= r1; r += 8) {
+                int v[8];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                a[(size_t)(r + q) * stride] = run;
-                run += v[q];
+                for (int q = 0; q < 8; ++q) v[q] = a[(size_t)(r + q) * stride];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    a[(size_t)(r + q) * stride] = run;
+                    run += v[q];
+                }
+            }
+            for (; r < r1; ++r) {
+                const int v = a[(size_t)r * stride];
+                a[(size_t)r * stride] = run;
+                run += v;
             }
         }
-        for (; r < r1; ++r) {
-            const int v = a[(size_t)r * stride];
-            a[(size_t)r * stride] = run;
-            run += v;
-        }
-        if (w == 3) p.o.rowtot[col] = run;
+        if (w == kScanWaves - 1) p.o.rowtot[col] = run;
     }
 }
 
@@ -426,7 +447,7 @@ hipError_t launch_shuffle(const moe_cfg& c, int nb, int tpb, const int32_t* row_
     p.o = o;
     // the histogram kernel also runs for T == 0 so the table it writes is zero
     hipLaunchKernelGGL(k_hist, dim3(nb), dim3(kThreads), 0, s, p);
-    hipLaunchKernelGGL(k_rowscan, dim3(ceil_div(p.nbk + c.P, 64)), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL(k_rowscan, dim3(ceil_div(p.nbk + c.P, 64)), dim3(64 * kScanWaves), 0, s, p);
     if (c.T > 0)
         hipLaunchKernelGGL(k_scatter, dim3(nb), dim3(kThreads), 0, s, p);
     else
