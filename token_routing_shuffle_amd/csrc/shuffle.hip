@@ -17,11 +17,11 @@
 // contiguous row of bucket counts per block); a column scan that turns each
 // bucket's per-block counts into offsets within the bucket (and the bucket's
 // total); a scatter whose blocks each scan the bucket totals (E*P of them)
-// into bucket starts in LDS (block 0 also writes the per-slot / per-group
-// results; an empty layer runs that scan as a kernel of its own) and rank
-// equal buckets inside a wave with ballots (stable: blocks, waves, chunks and
-// lanes all follow assignment order).  The global offset of (bucket k,
-// block b) is bucket_start[k] + (counts of k in blocks before b).
+// into bucket starts in LDS (one extra block writes the per-slot / per-group
+// results from the same scan; an empty layer runs that scan as a kernel of
+// its own) and rank equal buckets inside a wave with ballots (stable: blocks,
+// waves, chunks and lanes all follow assignment order).  The global offset of
+// (bucket k, block b) is bucket_start[k] + (counts of k in blocks before b).
 #include "common.h"
 #include "internal.h"
 
@@ -253,15 +253,17 @@ __global__ __launch_bounds__(kThreads) void k_scatter(ShParams p)
     const int nbk = p.nbk, P = p.P;
 
     // bucket and predicted-group starts: every block scans the bucket totals
-    // itself (E*P of them); block 0 also writes the offset tables
+    // itself (E*P of them); the extra last block writes the offset tables
     __shared__ int s_smem[17];
     __shared__ int s_start[kMaxBuckets + 1];
     __shared__ int s_tstart[65];
     __shared__ int s_gp[kMaxTPB];   // predicted group of each of the block's tokens
     bucket_starts<kThreads>(p, s_smem, s_start, s_tstart);
-    if (b == 0) {
+    if (b == p.nb) {
+        // the extra last block: the offset tables only (off the token
+        // blocks' critical path)
         write_offsets<kThreads>(p, s_start, s_tstart, &base[0][0]);
-        __syncthreads();   // its pair scratch (base) is zeroed below
+        return;
     }
     for (int i = threadIdx.x; i < nbk; i += kThreads) {
 #pragma unroll
@@ -448,8 +450,9 @@ hipError_t launch_shuffle(const moe_cfg& c, int nb, int tpb, const int32_t* row_
     // the histogram kernel also runs for T == 0 so the table it writes is zero
     hipLaunchKernelGGL(k_hist, dim3(nb), dim3(kThreads), 0, s, p);
     hipLaunchKernelGGL(k_rowscan, dim3(ceil_div(p.nbk + c.P, 64)), dim3(64 * kScanWaves), 0, s, p);
+    // one block per token block, plus one for the offset tables
     if (c.T > 0)
-        hipLaunchKernelGGL(k_scatter, dim3(nb), dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL(k_scatter, dim3(nb + 1), dim3(kThreads), 0, s, p);
     else
         hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, p);
     return hipGetLastError();
