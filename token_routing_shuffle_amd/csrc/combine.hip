@@ -51,19 +51,19 @@ __global__ __launch_bounds__(kThreads) void k_combine(int T, int H, const void* 
     float acc[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) acc[q] = 0.0f;
-    // rows of up to 8 assignments are loaded before they are summed, so
+    // rows of up to 16 assignments are loaded before they are summed, so
     // their memory latencies overlap; the sum stays in j order
-    for (int j8 = 0; j8 < kt; j8 += 8) {
-        u32x4_t v[8];
+    for (int j8 = 0; j8 < kt; j8 += 16) {
+        u32x4_t v[16];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 16; ++j) {
             if (j8 + j < kt) {
                 const int s = __builtin_amdgcn_readlane(my_s, j8 + j);
                 v[j] = __builtin_nontemporal_load(&((const u32x4_t*)ys)[(size_t)s * nch + c]);
             }
         }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < 16; ++j) {
             if (j8 + j < kt) {
                 const float wt = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(my_w), j8 + j));
                 if constexpr (BF16) {
