@@ -11,8 +11,9 @@
 //        gathered and restored to token order: out[tok_perm[i]] = y[i].
 //
 // Both are HBM-bound row moves: one wave per row, 16-byte lane accesses,
-// the partial rows of a chunk loaded before they are summed (in p order, in
-// fp32, rounded once to the output type).
+// the partial rows of a chunk (eight at a time, streaming loads and stores)
+// loaded before they are summed (in p order, in fp32, rounded once to the
+// output type).
 #include "common.h"
 #include "internal.h"
 
@@ -20,7 +21,7 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;   // 4 rows per block
-constexpr int kBatch = 4;       // partial rows in flight per chunk
+constexpr int kBatch = 8;       // partial rows in flight per chunk
 
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void k_srs(int T, int H, int n_part,
@@ -44,7 +45,7 @@ __global__ __launch_bounds__(kThreads) void k_srs(int T, int H, int n_part,
             u32x4_t v[kBatch];
 #pragma unroll
             for (int j = 0; j < kBatch; ++j)
-                if (p0 + j < n_part) v[j] = x[(size_t)(p0 + j) * part_stride + (size_t)t * nch + c];
+                if (p0 + j < n_part) v[j] = __builtin_nontemporal_load(&x[(size_t)(p0 + j) * part_stride + (size_t)t * nch + c]);
 #pragma unroll
             for (int j = 0; j < kBatch; ++j) {
                 if (p0 + j < n_part) {
@@ -76,7 +77,7 @@ __global__ __launch_bounds__(kThreads) void k_srs(int T, int H, int n_part,
 #pragma unroll
             for (int q = 0; q < 4; ++q) o[q] = __float_as_uint(acc[q]);
         }
-        y[(size_t)i * nch + c] = o;
+        __builtin_nontemporal_store(o, &y[(size_t)i * nch + c]);
     }
 }
 
