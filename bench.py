@@ -275,7 +275,8 @@ def main():
     alg = algorithmic(cfg, A, r["n_touched"])
     traffic, traffic_note = measured_traffic(args.workload)
     roofline = binding_roofline(alg["ffn_up_flops"], alg["ffn_up_bytes"], up_ms)
-    kname = "k_grouped_gemm<true,%d,%d>" % ((256, 256) if moe_wide(cfg) else (128, 384))
+    kname = "k_grouped_gemm<true,%d,%d,%s>" % (((256, 256) if moe_wide(cfg) else (128, 384))
+                                               + ("true" if moe_stream_weights(cfg) else "false",))
     roofline.update({"traffic": traffic, "traffic_unit": "bytes per launch", "traffic_source": traffic_note,
                      "kernel": kname + " (GEMM1 + SwiGLU, routed + shared)",
                      "touched_experts": r["n_touched"]})
@@ -345,6 +346,12 @@ def moe_wide(cfg):
     """256-wide GEMM1 tiles (2I and the shared 2*ns*Is multiples of 256)."""
     Ish = cfg.n_shared * cfg.I_shared
     return (2 * cfg.I) % 256 == 0 and (Ish == 0 or (2 * Ish) % 256 == 0)
+
+
+def moe_stream_weights(cfg):
+    """The library's rule for streaming the expert weights (non-temporal
+    loads): at most 64 routed rows per expert on average (decode batches)."""
+    return cfg.T * cfg.k <= 64 * cfg.E
 
 
 MALL_BYTES = 256 << 20

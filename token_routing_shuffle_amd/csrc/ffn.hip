@@ -111,7 +111,12 @@ MOE_DEV void acc_fence(f32x4_t& a, f32x4_t& b)
 // chunk, for either 32-wide k-half) are then free of bank conflicts.
 MOE_DEV int swz(int r, int c) { return c ^ (r & 7); }
 
-template <bool UP, int BN, int BMT>
+// SB: the weight operand is streamed -- loaded with the non-temporal cache
+// policy, for layers whose weight tiles are each read by one m-tile (decode
+// batches: a few rows per expert), where caching them only evicts lines that
+// are reused.  Measured on the DeepSeek-V3-shaped decode batch: GEMM1 2.33
+// -> 2.15 ms; on layers whose experts span several m-tiles it is slower.
+template <bool UP, int BN, int BMT, bool SB>
 __global__ __launch_bounds__(512, 1) void k_grouped_gemm(GemmParams p)
 {
     // tile rows at most: 256 (waves 2 x 4), or 384 with BN = 128 (waves 4 x 2)
@@ -412,7 +417,8 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm(GemmParams p)
                     if (q < NA)
                         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, MOE_LDS_PTR(dst), 16, doff[jj], ko, 0, 0);
                     else
-                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, MOE_LDS_PTR(dst), 16, doff[jj], kob, 0, 0);
+                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, MOE_LDS_PTR(dst), 16, doff[jj], kob, 0,
+                                                                 SB ? 2 : 0);  // 2: non-temporal
 #else
                     (void)dst;
                     (void)ko;
@@ -633,13 +639,13 @@ __global__ __launch_bounds__(64) void k_zero_ctr(int* ctr)
     if (threadIdx.x < 16) ctr[threadIdx.x] = 0;
 }
 
-template <bool UP, int BN, int BMT>
+template <bool UP, int BN, int BMT, bool SB>
 hipError_t launch_gemm_t(const GemmParams& p, long long ub, hipStream_t s)
 {
     // one resident block per CU (four LDS stages: 96 or 128 KB)
     long long grid = std::min<long long>(ub, (long long)num_cus());
     grid = (grid + 7) / 8 * 8;
-    hipLaunchKernelGGL((k_grouped_gemm<UP, BN, BMT>), dim3((unsigned)grid), dim3(512), 0, s, p);
+    hipLaunchKernelGGL((k_grouped_gemm<UP, BN, BMT, SB>), dim3((unsigned)grid), dim3(512), 0, s, p);
     return hipGetLastError();
 }
 
@@ -740,9 +746,15 @@ hipError_t launch_gemm(const moe_cfg& c, const FfnArgs& a, bool up, hipStream_t 
     if (a.n_routed > 0) ub += ((long long)ceil_div(a.A_max, TBM) + a.n_routed) * (nw_r / BN);
     if (p.has_shared) ub += (long long)ceil_div(c.T, TBM) * (nw_s / BN);
     if (ub == 0) return hipSuccess;
-    if (!wide)
-        return up ? launch_gemm_t<true, 128, 384>(p, ub, s) : launch_gemm_t<false, 128, 384>(p, ub, s);
-    return up ? launch_gemm_t<true, 256, 256>(p, ub, s) : launch_gemm_t<false, 256, 256>(p, ub, s);
+    // stream the weights when the routed experts average at most 64 rows
+    // (decode batches): then a weight tile is read by one m-tile
+    const bool sb = (long long)c.T * c.k_max <= 64LL * c.E;
+    if (!wide) {
+        if (sb) return up ? launch_gemm_t<true, 128, 384, true>(p, ub, s) : launch_gemm_t<false, 128, 384, true>(p, ub, s);
+        return up ? launch_gemm_t<true, 128, 384, false>(p, ub, s) : launch_gemm_t<false, 128, 384, false>(p, ub, s);
+    }
+    if (sb) return up ? launch_gemm_t<true, 256, 256, true>(p, ub, s) : launch_gemm_t<false, 256, 256, true>(p, ub, s);
+    return up ? launch_gemm_t<true, 256, 256, false>(p, ub, s) : launch_gemm_t<false, 256, 256, false>(p, ub, s);
 }
 
 hipError_t launch_f32(const moe_cfg& c, const FfnArgs& a, bool up, hipStream_t s)
