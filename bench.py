@@ -276,7 +276,7 @@ def main():
     traffic, traffic_note = measured_traffic(args.workload)
     roofline = binding_roofline(alg["ffn_up_flops"], alg["ffn_up_bytes"], up_ms)
     kname = "k_grouped_gemm<true,%d,%d,%s>" % (((256, 256) if moe_wide(cfg) else (128, 384))
-                                               + ("true" if moe_stream_weights(cfg) else "false",))
+                                               + ("true" if moe_stream_once(cfg) else "false",))
     roofline.update({"traffic": traffic, "traffic_unit": "bytes per launch", "traffic_source": traffic_note,
                      "kernel": kname + " (GEMM1 + SwiGLU, routed + shared)",
                      "touched_experts": r["n_touched"]})
@@ -348,10 +348,10 @@ def moe_wide(cfg):
     return (2 * cfg.I) % 256 == 0 and (Ish == 0 or (2 * Ish) % 256 == 0)
 
 
-def moe_stream_weights(cfg):
-    """The library's rule for streaming the expert weights (non-temporal
-    loads): at most 64 routed rows per expert on average (decode batches)."""
-    return cfg.T * cfg.k <= 64 * cfg.E
+def moe_stream_once(cfg):
+    """The library's rule for streaming weight tiles read once per call: the
+    routed experts' weights exceed 8x the 256 MB Infinity Cache."""
+    return 3.0 * cfg.E * cfg.I * cfg.H * 2 > 8.0 * (256 << 20)
 
 
 MALL_BYTES = 256 << 20

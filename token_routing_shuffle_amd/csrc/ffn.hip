@@ -111,12 +111,10 @@ MOE_DEV void acc_fence(f32x4_t& a, f32x4_t& b)
 // chunk, for either 32-wide k-half) are then free of bank conflicts.
 MOE_DEV int swz(int r, int c) { return c ^ (r & 7); }
 
-// SB: the weight operand is streamed -- loaded with the non-temporal cache
-// policy, for layers whose weight tiles are each read by one m-tile (decode
-// batches: a few rows per expert), where caching them only evicts lines that
-// are reused.  Measured on the DeepSeek-V3-shaped decode batch: GEMM1 2.33
-// -> 2.15 ms; on layers whose experts span several m-tiles it is slower.
-template <bool UP, int BN, int BMT, bool SB>
+// SO: the layer's weights far exceed the caches, so weight tiles read once per
+// call are streamed (see run_tile); without it the kernel is the same code
+// with the default cache policy everywhere.
+template <bool UP, int BN, int BMT, bool SO>
 __global__ __launch_bounds__(512, 1) void k_grouped_gemm(GemmParams p)
 {
     // tile rows at most: 256 (waves 2 x 4), or 384 with BN = 128 (waves 4 x 2)
@@ -366,7 +364,13 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm(GemmParams p)
         // split between the two wave rows.  The DMA loads the A rows in
         // groups of 64 (kAload), so for odd RT the last 32 rows loaded are
         // not used by the MFMAs.
-        auto run_tile = [&](auto rt_tag) {
+        // STB: the weight tiles are streamed (non-temporal loads).  Chosen for
+        // a segment of one m-tile, which reads each of its weight tiles once,
+        // when the layer's weights far exceed the caches (SO): such a tile is
+        // gone from the Infinity Cache by the next call, and caching it only
+        // evicts the activation rows and intermediates that are reused.
+        auto run_tile = [&](auto rt_tag, auto stb_tag) {
+            constexpr bool STB = decltype(stb_tag)::value != 0;
             constexpr int RT = decltype(rt_tag)::value;
             constexpr int kArows = RT * kHq;                 // A rows of the tile
             constexpr int kAload = (kArows + 63) / 64 * 64;  // A rows loaded
@@ -418,7 +422,7 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm(GemmParams p)
                         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, MOE_LDS_PTR(dst), 16, doff[jj], ko, 0, 0);
                     else
                         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsB, MOE_LDS_PTR(dst), 16, doff[jj], kob, 0,
-                                                                 SB ? 2 : 0);  // 2: non-temporal
+                                                                 STB ? 2 : 0);  // 2: non-temporal
 #else
                     (void)dst;
                     (void)ko;
@@ -547,23 +551,31 @@ __global__ __launch_bounds__(512, 1) void k_grouped_gemm(GemmParams p)
                 __syncthreads();
             }
         };
+        auto go = [&](auto rt_tag) {
+            if constexpr (SO) {
+                if (mt == 1) run_tile(rt_tag, IntC<1>{});
+                else run_tile(rt_tag, IntC<0>{});
+            } else {
+                run_tile(rt_tag, IntC<0>{});
+            }
+        };
         if constexpr (BM == 384) {
             const int rt = hgt / 64;
-            if (rt >= 6) run_tile(IntC<6>{});
-            else if (rt == 5) run_tile(IntC<5>{});
-            else if (rt == 4) run_tile(IntC<4>{});
-            else if (rt == 3) run_tile(IntC<3>{});
-            else if (rt == 2) run_tile(IntC<2>{});
-            else run_tile(IntC<1>{});
+            if (rt >= 6) go(IntC<6>{});
+            else if (rt == 5) go(IntC<5>{});
+            else if (rt == 4) go(IntC<4>{});
+            else if (rt == 3) go(IntC<3>{});
+            else if (rt == 2) go(IntC<2>{});
+            else go(IntC<1>{});
         } else {
-            if (hgt > 224) run_tile(IntC<8>{});
-            else if (hgt > 192) run_tile(IntC<7>{});
-            else if (hgt > 160) run_tile(IntC<6>{});
-            else if (hgt > 128) run_tile(IntC<5>{});
-            else if (hgt > 96) run_tile(IntC<4>{});
-            else if (hgt > 64) run_tile(IntC<3>{});
-            else if (hgt > 32) run_tile(IntC<2>{});
-            else run_tile(IntC<1>{});
+            if (hgt > 224) go(IntC<8>{});
+            else if (hgt > 192) go(IntC<7>{});
+            else if (hgt > 160) go(IntC<6>{});
+            else if (hgt > 128) go(IntC<5>{});
+            else if (hgt > 96) go(IntC<4>{});
+            else if (hgt > 64) go(IntC<3>{});
+            else if (hgt > 32) go(IntC<2>{});
+            else go(IntC<1>{});
         }
     }
 }
@@ -639,13 +651,13 @@ __global__ __launch_bounds__(64) void k_zero_ctr(int* ctr)
     if (threadIdx.x < 16) ctr[threadIdx.x] = 0;
 }
 
-template <bool UP, int BN, int BMT, bool SB>
+template <bool UP, int BN, int BMT, bool SO>
 hipError_t launch_gemm_t(const GemmParams& p, long long ub, hipStream_t s)
 {
     // one resident block per CU (four LDS stages: 96 or 128 KB)
     long long grid = std::min<long long>(ub, (long long)num_cus());
     grid = (grid + 7) / 8 * 8;
-    hipLaunchKernelGGL((k_grouped_gemm<UP, BN, BMT, SB>), dim3((unsigned)grid), dim3(512), 0, s, p);
+    hipLaunchKernelGGL((k_grouped_gemm<UP, BN, BMT, SO>), dim3((unsigned)grid), dim3(512), 0, s, p);
     return hipGetLastError();
 }
 
@@ -746,14 +758,14 @@ hipError_t launch_gemm(const moe_cfg& c, const FfnArgs& a, bool up, hipStream_t 
     if (a.n_routed > 0) ub += ((long long)ceil_div(a.A_max, TBM) + a.n_routed) * (nw_r / BN);
     if (p.has_shared) ub += (long long)ceil_div(c.T, TBM) * (nw_s / BN);
     if (ub == 0) return hipSuccess;
-    // stream the weights when the routed experts average at most 64 rows
-    // (decode batches): then a weight tile is read by one m-tile
-    const bool sb = (long long)c.T * c.k_max <= 64LL * c.E;
+    // the routed experts' weights (3 I x H each) more than 8x the 256 MB
+    // Infinity Cache: a weight tile read once is not found in it again
+    const bool so = 3.0 * c.E * c.I * c.H * 2 > 8.0 * (256 << 20);
     if (!wide) {
-        if (sb) return up ? launch_gemm_t<true, 128, 384, true>(p, ub, s) : launch_gemm_t<false, 128, 384, true>(p, ub, s);
+        if (so) return up ? launch_gemm_t<true, 128, 384, true>(p, ub, s) : launch_gemm_t<false, 128, 384, true>(p, ub, s);
         return up ? launch_gemm_t<true, 128, 384, false>(p, ub, s) : launch_gemm_t<false, 128, 384, false>(p, ub, s);
     }
-    if (sb) return up ? launch_gemm_t<true, 256, 256, true>(p, ub, s) : launch_gemm_t<false, 256, 256, true>(p, ub, s);
+    if (so) return up ? launch_gemm_t<true, 256, 256, true>(p, ub, s) : launch_gemm_t<false, 256, 256, true>(p, ub, s);
     return up ? launch_gemm_t<true, 256, 256, false>(p, ub, s) : launch_gemm_t<false, 256, 256, false>(p, ub, s);
 }
 
