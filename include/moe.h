@@ -296,6 +296,10 @@ int32_t moe_shuffle_noalloc(const moe_cfg* cfg, const int32_t* row_ptr, const in
  *   W13 = Wsh13[2*ns*Is, H] (all W1 rows, then all W3 rows), W2 = Wsh2[H, ns*Is];
  *   y[T,H].  x_sorted, sorted_to_assign, row_ptr, expert_off, e_begin, e_end
  *   are ignored.
+ * Nothing to compute (T = 0, or an empty slot range): returns MOE_OK after
+ * checking cfg, which, the weights, y and the workspace, without reading
+ * the row arguments (x, x_sorted, row_ptr, sorted_to_assign, expert_off),
+ * which may then be NULL.
  * Workspace: required.
  */
 int32_t moe_expert_ffn(const moe_cfg* cfg, int32_t which, const void* x_sorted, const void* x,

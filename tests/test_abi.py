@@ -258,6 +258,29 @@ def test_workspace_grows_with_tokens_and_shrinks_with_fused_gather(m):
     assert m.moe_workspace_bytes(c2) - m.moe_workspace_bytes(c3) == 2048 * 8 * 2048 * 2
 
 
+def test_expert_ffn_empty_layer_reads_no_rows(m):
+    """T = 0 (or an empty slot range): moe_expert_ffn returns MOE_OK with the
+    row arguments NULL, after checking the rest; nothing is launched."""
+    from token_routing_shuffle_amd import workload as wl
+    L = m.lib()
+    fake = ctypes.c_void_p(0x1000)       # never dereferenced
+    c = m.make_cfg(wl.CONFIGS["dsv2lite"], T=0)
+    ws_bytes = max(m.moe_workspace_bytes(c), 256)
+    for which in (m.MOE_FFN_ROUTED, m.MOE_FFN_SHARED):
+        assert L.moe_expert_ffn(ctypes.byref(c), which, None, None, None, None, None, fake, fake, 0, c.E,
+                                fake, fake, ws_bytes, None) == m.MOE_OK
+    # the weights are still checked
+    assert L.moe_expert_ffn(ctypes.byref(c), m.MOE_FFN_ROUTED, None, None, None, None, None, None, fake, 0,
+                            c.E, fake, fake, ws_bytes, None) == m.MOE_EINVAL
+    # an empty slot range of a non-empty layer
+    c1 = m.make_cfg(wl.CONFIGS["dsv2lite"])
+    ws1 = m.moe_workspace_bytes(c1)
+    assert L.moe_expert_ffn(ctypes.byref(c1), m.MOE_FFN_ROUTED, None, None, None, None, None, fake, fake, 5, 5,
+                            fake, fake, ws1, None) == m.MOE_OK
+    assert L.moe_expert_ffn(ctypes.byref(c1), m.MOE_FFN_ROUTED, None, None, None, None, None, fake, fake, 0, 5,
+                            fake, fake, ws1, None) == m.MOE_EINVAL
+
+
 def test_empty_layer_validates(m):
     from token_routing_shuffle_amd import workload as wl
     c = m.make_cfg(wl.CONFIGS["tiny"], T=0)

@@ -429,9 +429,9 @@ MOE_API int32_t moe_expert_ffn(const moe_cfg* cfg, int32_t which, const void* x_
     a.ctr = at<int32_t>(ws, L.gemm_ctr);
     if (which == MOE_FFN_SHARED) {
         if (c.n_shared == 0) return fail(MOE_ESHAPE, "no shared experts in cfg");
+        if (c.T == 0) return MOE_OK;  // nothing to read or write
         REQUIRE(x);
         REQUIRE16(x);
-        if (c.T == 0) return MOE_OK;
         a.n_routed = 0;
         a.sh_x = x;
         a.sh_W13 = W13;
@@ -441,6 +441,7 @@ MOE_API int32_t moe_expert_ffn(const moe_cfg* cfg, int32_t which, const void* x_
         a.Ish = c.n_shared * c.I_shared;
     } else {
         if (e_begin < 0 || e_end > c.E || e_begin > e_end) return fail(MOE_EINVAL, "bad expert range");
+        if (c.T == 0 || e_begin == e_end) return MOE_OK;  // nothing to read or write
         REQUIRE(expert_off);
         if (x_sorted == nullptr) {
             REQUIRE(x);
@@ -450,7 +451,6 @@ MOE_API int32_t moe_expert_ffn(const moe_cfg* cfg, int32_t which, const void* x_
         } else {
             REQUIRE16(x_sorted);
         }
-        if (c.T == 0 || e_begin == e_end) return MOE_OK;
         a.n_routed = e_end - e_begin;
         a.e_begin = e_begin;
         a.expert_off = expert_off;
