@@ -40,7 +40,13 @@
 //   barrier (every wave has read stage kt & 1); DMA step kt+2 into it
 //   MFMAs of half 1
 // so a DMA has about one and a half k-steps to land and up to two stages
-// (128 KB per CU) are in flight.
+// (128 KB per CU) are in flight.  The partial wait (vmcnt(NI): the DMA of
+// step kt+1 may still be in flight) relies on the LDS DMA loads retiring in
+// order among themselves.  Loads into registers do not retire in order
+// relative to them (measured: with such loads counted in the allowance, LDS
+// reads ran ahead of the DMA now and then), so none is issued between a DMA
+// and the wait that counts it; a gathered tile's row-index loads all come
+// before its first DMA.
 #include <atomic>
 
 #include "common.h"

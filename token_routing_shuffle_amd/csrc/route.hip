@@ -142,7 +142,9 @@ __global__ __launch_bounds__(256) void k_gate_logits(int T, int H, int E, int Kc
     dma(0);
     if (nch > 1) dma(1);
     for (int c = 0; c < nch; ++c) {
-        // this wave's DMA of chunk c has landed (chunk c+1's may be in flight)
+        // this wave's DMA of chunk c has landed (chunk c+1's may be in flight;
+        // a partial count is sound because only LDS DMA loads, which retire in
+        // order among themselves, are issued in this loop)
         if (c + 1 < nch) wait_vmcnt<kGNI>(); else wait_vmcnt<0>();
         __builtin_amdgcn_s_barrier();  // chunk c visible; chunk c-1's buffer free
         if (c + 2 < nch) dma(c + 2);
