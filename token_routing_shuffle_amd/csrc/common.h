@@ -118,6 +118,29 @@ MOE_DEV uint64_t wave_max_u64(uint64_t v)
     return ((uint64_t)hi << 32) | lo;
 }
 
+// Maximum of a 64-bit value over aligned segments of L lanes (L a power of
+// two from 1 to 64), returned to every lane of its segment.  All 64 lanes
+// must be active.  Within a row: quad swaps (lane ^ 1, lane ^ 2), then the
+// half-row and row mirrors, which pair each quad (half-row) with the other
+// of its half-row (row); across rows, lane ^ 16 and lane ^ 32 by permute.
+MOE_DEV uint64_t seg_max_u64(uint64_t v, int L)
+{
+    if (L >= 2) v = dpp_max_u64<0xB1, 0xF>(v);
+    if (L >= 4) v = dpp_max_u64<0x4E, 0xF>(v);
+    if (L >= 8) v = dpp_max_u64<0x141, 0xF>(v);
+    if (L >= 16) v = dpp_max_u64<0x140, 0xF>(v);
+#pragma unroll
+    for (int o = 16; o <= 32; o <<= 1) {
+        if (L > o) {
+            const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, o);
+            const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), o);
+            const uint64_t w = ((uint64_t)hi << 32) | lo;
+            v = w > v ? w : v;
+        }
+    }
+    return v;
+}
+
 MOE_DEV int wave_incl_scan(int v)
 {
     const int l = lane_id();
@@ -235,6 +258,12 @@ MOE_DEV uint32_t ordered_key(float f)
     const float g = f + 0.0f;  // -0 + 0 = +0 under round-to-nearest
     const uint32_t u = __float_as_uint(g);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inverse of ordered_key (a key of -0 comes back as +0).
+MOE_DEV float unordered_key(uint32_t k)
+{
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
 }
 
 // ---------------------------------------------------------------------------

@@ -187,7 +187,6 @@ __global__ __launch_bounds__(kThreads) void k_route(RouteParams p)
     __shared__ int s_s2o[EP];
     __shared__ int s_o2s[EP];
     __shared__ float s_key[kWaves][EP];
-    __shared__ float s_gs[kWaves][64];
     constexpr int kSK = NTW >= kWaves ? 1 : kWaves / NTW;
     __shared__ float s_part[kSK > 1 ? kSK : 1][kBM][kSK > 1 ? EP : 1];
 
@@ -239,16 +238,41 @@ __global__ __launch_bounds__(kThreads) void k_route(RouteParams p)
 
     // ---------------- gate GEMM: logits[16 tokens][E] ----------------
     if (p.glog != nullptr) {
-        // from the tiled gate GEMM: partial sums added in slice order
-        for (int idx = tid; idx < kBM * EP; idx += kThreads) {
+        // from the tiled gate GEMM: partial sums added in slice order, eight
+        // loads in flight per lane (kPer elements, kQ slices of each)
+        static_assert(kBM * EP % kThreads == 0, "whole elements per thread");
+        constexpr int kPer = kBM * EP / kThreads;
+        constexpr int kQ = kPer >= 8 ? 1 : 8 / kPer;
+        const size_t sstride = (size_t)T * E;
+        float sum[kPer];
+        size_t off[kPer];
+        bool in[kPer];
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int idx = tid + u * kThreads;
             const int row = idx / EP, col = idx % EP;
             const int t = t0 + row;
-            float sum = 0.0f;
-            if (t < T && col < E) {
-                sum = p.glog[(size_t)t * E + col];
-                for (int q = 1; q < p.gS; ++q) sum += p.glog[((size_t)q * T + t) * E + col];
-            }
-            s_log[row][col] = sum;
+            in[u] = t < T && col < E;
+            off[u] = in[u] ? (size_t)t * E + col : 0;
+            sum[u] = in[u] ? p.glog[off[u]] : 0.0f;
+        }
+        for (int q0 = 1; q0 < p.gS; q0 += kQ) {
+            float v[kPer][kQ];
+#pragma unroll
+            for (int u = 0; u < kPer; ++u)
+#pragma unroll
+                for (int q = 0; q < kQ; ++q)
+                    v[u][q] = (in[u] && q0 + q < p.gS) ? p.glog[(size_t)(q0 + q) * sstride + off[u]] : 0.0f;
+#pragma unroll
+            for (int u = 0; u < kPer; ++u)
+#pragma unroll
+                for (int q = 0; q < kQ; ++q)
+                    if (q0 + q < p.gS) sum[u] += v[u][q];
+        }
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int idx = tid + u * kThreads;
+            s_log[idx / EP][idx % EP] = sum[u];
         }
     } else if constexpr (BF16 && kBM == 16) {
         // MFMA 16x16x32 bf16.  Lane l feeds token row (l & 15) and expert
@@ -393,44 +417,55 @@ __global__ __launch_bounds__(kThreads) void k_route(RouteParams p)
             }
         }
         if (grouped) {
+            // keys in original-id order, so that a routing group (a block of
+            // gsize consecutive original ids) is a contiguous range
 #pragma unroll
             for (int i = 0; i < NTW; ++i)
                 if (ok[i]) s_key[w][oid[i]] = key[i];
-            __syncthreads();
-            if (l < p.n_rgroups) {
-                // sum of the rgroup_topn largest keys, largest first
-                float top[8];
-                const int n = p.rgroup_topn;
-                for (int q = 0; q < 8; ++q) top[q] = -__builtin_inff();
-                for (int e = 0; e < gsize; ++e) {
-                    float v = s_key[w][l * gsize + e];
-                    for (int q = 0; q < 8; ++q) {
-                        if (q < n && v > top[q]) {
-                            const float tmp = top[q];
-                            top[q] = v;
-                            v = tmp;
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            // Group scores: L lanes per group (L * n_rgroups <= 64, L a power
+            // of two), each scanning m of its group's keys as (key, original
+            // id) candidates.  Round j takes the group maximum over the
+            // segment and its owner marks it taken: the rgroup_topn largest
+            // keys in descending order, added in that order.
+            const int G = p.n_rgroups;
+            int G2 = 1;
+            while (G2 < G) G2 <<= 1;
+            const int L = 64 / G2;
+            const int m = (gsize + L - 1) / L;
+            const int g = l / L, sub = l % L;
+            const int first = g * gsize + sub * m;
+            const int mine = g < G ? max(0, min(m, gsize - sub * m)) : 0;  // keys this lane scans
+            uint32_t taken = 0;
+            float sc = 0.0f;
+            for (int j = 0; j < p.rgroup_topn; ++j) {
+                uint64_t b = 0ull;
+                int be = 0;
+#pragma unroll 4
+                for (int e = 0; e < mine; ++e) {
+                    if (!((taken >> e) & 1u)) {
+                        const uint64_t c = ((uint64_t)ordered_key(s_key[w][first + e]) << 32) |
+                                           (0xFFFFFFFFu - (uint32_t)(first + e));
+                        if (c > b) {
+                            b = c;
+                            be = e;
                         }
                     }
                 }
-                float sc = top[0];
-                for (int q = 1; q < 8; ++q)
-                    if (q < n) sc = sc + top[q];
-                s_gs[w][l] = sc;
+                const uint64_t gb = seg_max_u64(b, L);
+                if (b == gb && b != 0ull) taken |= 1u << be;
+                const float v = unordered_key((uint32_t)(gb >> 32));
+                sc = j == 0 ? v : sc + v;
             }
-            __syncthreads();
+            // topk_rgroups rounds of the wave maximum over (score, lower
+            // group id first), one candidate per group
+            uint64_t gk = (g < G && sub == 0) ? ((uint64_t)ordered_key(sc) << 32) | (0xFFFFFFFFu - (uint32_t)g) : 0ull;
             uint64_t kept = 0;
             for (int j = 0; j < p.topk_rgroups; ++j) {
-                int best = -1;
-                float bs = 0.0f;
-                for (int g = 0; g < p.n_rgroups; ++g) {
-                    if ((kept >> g) & 1ull) continue;
-                    const float sc = s_gs[w][g];
-                    if (best < 0 || sc > bs) {
-                        best = g;
-                        bs = sc;
-                    }
-                }
-                kept |= 1ull << best;
+                const uint64_t b = wave_max_u64(gk);
+                if (gk == b) gk = 0ull;
+                kept |= 1ull << (0xFFFFFFFFu - (uint32_t)b);
             }
 #pragma unroll
             for (int i = 0; i < NTW; ++i) ok[i] = ok[i] && ((kept >> (oid[i] / gsize)) & 1ull);
