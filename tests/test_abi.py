@@ -247,6 +247,26 @@ def test_route_workspace(m):
     assert m.moe_route_workspace_bytes(bad) == 0
 
 
+def test_route_workspace_gate_slices(m):
+    """The route workspace holds the tiled gate GEMM's K slices of partial
+    logits, S * T * E fp32 after the dispatch tables.  Layers with at least
+    32 tiles of 128 tokens x 256 experts (128 when E < 256) take those wide
+    tiles, others 64 x 128 tiles; S doubles while the blocks number under
+    256 and each slice keeps at least four 64-wide chunks."""
+    from token_routing_shuffle_amd import workload as wl
+    for name, T, over, S in [("dsv3_prefill", 8192, {}, 4),      # 64 wide tiles
+                             ("dsv3_prefill", 4097, {}, 8),      # 33 wide tiles
+                             ("qwen3", 16384, {}, 2),            # 128 wide tiles of 128 experts
+                             ("qwen3", 4100, dict(E=192, P=3), 4),  # 33 x 2, partial expert tile
+                             ("prism", 8192, {}, 2),             # 64 x 2
+                             ("prism", 4160, {}, 4),             # 33 x 2
+                             ("dsv3_decode", 256, {}, 16),       # 2 wide tiles: 4 x 2 narrow ones
+                             ("qwen3", 300, dict(E=192, P=3), 8)]:  # 5 x 2 narrow ones
+        c = m.make_cfg(wl.CONFIGS[name], T=T, **over)
+        n = m.moe_route_workspace_bytes(c)
+        assert n // (T * c.E * 4) == S, (name, T, over, n)
+
+
 def test_workspace_grows_with_tokens_and_shrinks_with_fused_gather(m):
     from token_routing_shuffle_amd import workload as wl
     c1 = m.make_cfg(wl.CONFIGS["qwen3"], T=1024)

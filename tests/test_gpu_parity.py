@@ -116,6 +116,30 @@ def test_route(key):
     assert (np.abs(w_gpu - w_or)[same] <= tol[same]).all()
 
 
+# Layers with enough tokens for the gate GEMM's wide tiles (128 tokens x
+# 128 or 256 experts), with a ragged last token tile and, for E = 192, a
+# partial expert tile; K split 4 or 8 (the route workspace test in the ABI
+# suite checks which tiling each shape takes).
+WIDE_GATE = {
+    "wide_E192": ("qwen3", 4100, dict(E=192, P=3)),
+    "wide_dsv3": ("dsv3_prefill", 4097, {}),
+    "wide_prism": ("prism", 4160, {}),
+}
+
+
+@pytest.mark.parametrize("key", list(WIDE_GATE))
+def test_route_wide_gate(key):
+    name, T, over = WIDE_GATE[key]
+    c = hn.make_case(name, T, profile_tokens=1024, **over)
+    g = gpu_route(c)
+    l_gpu32 = hn.logits_orig(c, g["logits"].reshape(-1))
+    l64 = hn.oracle_logits(c)
+    assert (np.abs(l_gpu32 - l64) <= hn.logit_bound(c)).all()
+    st = hn.strict_route_parity(c, g["row_ptr"], g["slot"], g["w"], l_gpu32, "wide gate " + key)
+    hn.report("[route] %s: T=%d E=%d selection bit-exact on the GPU logits (%d exact-tie tokens), "
+              "max |dl| = %.3g" % (key, T, c.cfg.E, st["ties"], np.abs(l_gpu32 - l64).max()))
+
+
 @pytest.mark.parametrize("key", list(CASES))
 def test_shuffle_bit_exact(key):
     c = case(key)

@@ -177,6 +177,119 @@ __global__ __launch_bounds__(256) void k_gate_logits(int T, int H, int E, int Kc
     }
 }
 
+// The same gate GEMM in 128-token x TE-expert tiles (TE = 128 or 256) for
+// layers with enough tiles to fill the chip: per 64-wide k-chunk a block
+// loads (128 + TE) rows for 128 * TE outputs, against 192 rows for 64 * 128
+// above, which halves the bytes through the LDS DMA path (the bound of
+// both) at TE = 256.  Eight waves as 2 (tokens) x 4 (experts), each owning
+// a 64 x TE/4 block of 16x16 MFMA tiles; three chunk buffers (144 KB at
+// TE = 256, one block per CU), the same row swizzle and DMA ordering.
+constexpr int kBT = 128;
+
+template <int TE>
+__global__ __launch_bounds__(512) void k_gate_logits_wide(int T, int H, int E, int Kc, const uint16_t* x,
+                                                          const uint16_t* Wg, float* __restrict__ glog)
+{
+    constexpr int kRows = kBT + TE;          // LDS rows per chunk
+    constexpr int kChunkE = kRows * 64;      // bf16 elements per chunk buffer
+    constexpr int kNI = kRows / 8 / 8;       // DMA instructions per wave per chunk
+    constexpr int RM = 4, RN = TE / 64;      // 16x16 tiles per wave: 64 tokens x TE/4 experts
+    __shared__ __attribute__((aligned(16))) uint16_t s_g[kGNB * kChunkE];
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63;
+    const int wm = w >> 2, wn = w & 3;
+    const int t0 = blockIdx.x * kBT, e0 = blockIdx.y * TE, ks = blockIdx.z;
+    const int nch = Kc / 64;
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, T * H * 2, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rw = __builtin_amdgcn_make_buffer_rsrc((void*)Wg, (short)0, E * H * 2, 0x00020000);
+    // DMA instruction q = w * kNI + j covers LDS rows 8q..8q+7 (x rows
+    // first, then Wg rows); lane l fills row 8q + (l >> 3) at slot l & 7,
+    // which holds the row's global chunk (l & 7) ^ (row & 7).  Rows past T
+    // or E repeat the last one.
+    int doff[kNI];
+#pragma unroll
+    for (int j = 0; j < kNI; ++j) {
+        const int q = w * kNI + j;
+        const int row = q * 8 + (l >> 3);
+        const int chunk = (l & 7) ^ (row & 7);
+        const int src = row < kBT ? min(t0 + row, T - 1) : min(e0 + row - kBT, E - 1);
+        doff[j] = src * H * 2 + chunk * 16;
+    }
+    auto dma = [&](int c) {
+        const int ko = (ks * Kc + c * 64) * 2;
+        uint16_t* buf = s_g + (c % kGNB) * kChunkE;
+#pragma unroll
+        for (int j = 0; j < kNI; ++j) {
+            const int q = w * kNI + j;
+            uint16_t* dst = buf + q * 8 * 64;
+#if defined(__HIP_DEVICE_COMPILE__)  // the host pass cannot form LDS pointers
+            if (q * 8 < kBT)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, MOE_LDS_PTR(dst), 16, doff[j], ko, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, MOE_LDS_PTR(dst), 16, doff[j], ko, 0, 0);
+#else
+            (void)dst;
+            (void)ko;
+#endif
+        }
+    };
+    // Fragments: lane (r = l & 15, kg = l >> 4) reads row r of each 16-row
+    // block at chunks kg (first 32-wide half) and kg + 4 (second half).
+    const int r = l & 15, kg = l >> 4;
+    const uint32_t sbase = lds_addr(s_g);
+    const uint32_t a_row = sbase + (wm * 64 + r) * 128, b_row = sbase + (kBT + wn * (TE / 4) + r) * 128;
+    const uint32_t c0 = (uint32_t)((kg ^ (r & 7)) << 4), c1 = (uint32_t)(((kg + 4) ^ (r & 7)) << 4);
+    f32x4_t acc[RM][RN];
+#pragma unroll
+    for (int i = 0; i < RM; ++i)
+#pragma unroll
+        for (int j = 0; j < RN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+    dma(0);
+    if (nch > 1) dma(1);
+    for (int c = 0; c < nch; ++c) {
+        // this wave's DMA of chunk c has landed (chunk c+1's may be in
+        // flight; only LDS DMA loads are issued in this loop, and they retire
+        // in order among themselves)
+        if (c + 1 < nch) wait_vmcnt<kNI>(); else wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();  // chunk c visible; chunk c-1's buffer free
+        if (c + 2 < nch) dma(c + 2);
+        const uint32_t so = (uint32_t)((c % kGNB) * kChunkE * 2);
+        bf16x8_t a[2 * RM], b[2 * RN];
+        static_for<0, RM>([&](auto it) {
+            constexpr int i = it.value;
+            a[2 * i] = lds_read_b128<i * 16 * 128>(a_row + so + c0);
+            a[2 * i + 1] = lds_read_b128<i * 16 * 128>(a_row + so + c1);
+        });
+        static_for<0, RN>([&](auto it) {
+            constexpr int j = it.value;
+            b[2 * j] = lds_read_b128<j * 16 * 128>(b_row + so + c0);
+            b[2 * j + 1] = lds_read_b128<j * 16 * 128>(b_row + so + c1);
+        });
+        frag_wait(a, b);
+#pragma unroll
+        for (int i = 0; i < RM; ++i)
+#pragma unroll
+            for (int j = 0; j < RN; ++j) {
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2 * i], b[2 * j], acc[i][j], 0, 0, 0);
+                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2 * i + 1], b[2 * j + 1], acc[i][j], 0, 0, 0);
+            }
+    }
+    // D layout: lane l holds expert column (l & 15) of tile (i, j), tokens 4*kg + v
+    float* out = glog + (size_t)ks * T * E;
+#pragma unroll
+    for (int i = 0; i < RM; ++i)
+#pragma unroll
+        for (int j = 0; j < RN; ++j) {
+            const int e = e0 + wn * (TE / 4) + j * 16 + r;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int t = t0 + wm * 64 + i * 16 + kg * 4 + v;
+                if (t < T && e < E) out[(size_t)t * E + e] = acc[i][j][v];
+            }
+        }
+}
+
 template <int NTW, bool BF16>
 __global__ __launch_bounds__(kThreads) void k_route(RouteParams p)
 {
@@ -601,11 +714,25 @@ hipError_t launch_row_ptr(const moe_cfg& c, const int32_t* k_tok, int32_t* row_p
 // kernel clamps a partial 128-expert tile and writes only e < E.
 bool gate_tiled(const moe_cfg& c) { return c.dtype == MOE_BF16 && c.E > 64; }
 
+namespace {
+// Expert width of the wide gate tiles (0: the 64 x 128 tiles), chosen when
+// the layer has at least 32 wide tiles, so that a K split of at most eight
+// fills the chip.
+int gate_wide(const moe_cfg& c)
+{
+    const int te = c.E >= 256 ? 256 : 128;
+    const long long tiles = (long long)ceil_div(c.T, kBT) * ceil_div(c.E, te);
+    return tiles >= 32 ? te : 0;
+}
+}  // namespace
+
 int gate_split(const moe_cfg& c)
 {
     // K slices: enough blocks for the chip (256 CUs), each slice at least
     // four 64-wide chunks; the partial sums are added in slice order.
-    const long long tiles = (long long)ceil_div(c.T, kGT) * ceil_div(c.E, kGE);
+    const int te = gate_wide(c);
+    const long long tiles = te ? (long long)ceil_div(c.T, kBT) * ceil_div(c.E, te)
+                               : (long long)ceil_div(c.T, kGT) * ceil_div(c.E, kGE);
     const int nch = c.H / 64;
     int S = 1;
     while (tiles * S < 256 && nch % (2 * S) == 0 && nch / (2 * S) >= 4) S *= 2;
@@ -649,8 +776,16 @@ hipError_t launch_route(const moe_cfg& c, const void* x, const void* Wg, const f
     p.gS = 1;
     if (gate_tiled(c)) {
         const int S = gate_split(c);
-        hipLaunchKernelGGL(k_gate_logits, dim3(ceil_div(c.T, kGT), ceil_div(c.E, kGE), S), dim3(256), 0, s,
-                           c.T, c.H, c.E, c.H / S, (const uint16_t*)x, (const uint16_t*)Wg, glog);
+        const int te = gate_wide(c);
+        if (te == 256)
+            hipLaunchKernelGGL(k_gate_logits_wide<256>, dim3(ceil_div(c.T, kBT), ceil_div(c.E, 256), S), dim3(512),
+                               0, s, c.T, c.H, c.E, c.H / S, (const uint16_t*)x, (const uint16_t*)Wg, glog);
+        else if (te == 128)
+            hipLaunchKernelGGL(k_gate_logits_wide<128>, dim3(ceil_div(c.T, kBT), ceil_div(c.E, 128), S), dim3(512),
+                               0, s, c.T, c.H, c.E, c.H / S, (const uint16_t*)x, (const uint16_t*)Wg, glog);
+        else
+            hipLaunchKernelGGL(k_gate_logits, dim3(ceil_div(c.T, kGT), ceil_div(c.E, kGE), S), dim3(256), 0, s,
+                               c.T, c.H, c.E, c.H / S, (const uint16_t*)x, (const uint16_t*)Wg, glog);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         p.glog = glog;
