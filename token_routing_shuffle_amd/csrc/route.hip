@@ -12,6 +12,18 @@
 namespace moe {
 namespace {
 
+// Maximum of a 32-bit value over the wave, returned to every lane (all 64
+// lanes active): quad swaps and the half-row and row mirrors leave each
+// row's maximum in all its lanes, then the four rows' are combined.
+MOE_DEV uint32_t wave_max_u32(uint32_t v)
+{
+    v = max(v, dpp_u32<0xB1>(v));
+    v = max(v, dpp_u32<0x4E>(v));
+    v = max(v, dpp_u32<0x141>(v));
+    v = max(v, dpp_u32<0x140>(v));
+    return max(max(readlane_u32(v, 0), readlane_u32(v, 16)), max(readlane_u32(v, 32), readlane_u32(v, 48)));
+}
+
 // Tokens per route block: 16 (one MFMA row tile) when the kernel computes
 // the gate itself (E <= 64), 8 when it only sums the tiled gate kernel's
 // partial logits and selects (E > 64): one token per wave, twice the blocks.
@@ -510,7 +522,7 @@ __global__ __launch_bounds__(kThreads) void k_route(RouteParams p)
         const int row = w + kWaves * it;
         const int t = t0 + row;
         const bool active = t < T;  // wave-uniform
-        const int kt = s_kt[row];
+        const int kt = __builtin_amdgcn_readfirstlane(s_kt[row]);  // one token per wave
         (void)active;
 
         float lg[NTW], key[NTW];
@@ -589,7 +601,9 @@ __global__ __launch_bounds__(kThreads) void k_route(RouteParams p)
         // (key desc, original id asc) winner; 0 marks no candidate (every
         // real key's upper half is nonzero).  Each lane sorts its NTW keys
         // descending; a round takes the wave maximum of the lanes' heads and
-        // the lane holding it drops its head.
+        // the lane holding it drops its head.  The maximum is found on the
+        // upper (key) halves; the lower (id) halves are compared only when
+        // several heads share the largest key.
         uint64_t pk[NTW];
 #pragma unroll
         for (int i = 0; i < NTW; ++i)
@@ -605,13 +619,24 @@ __global__ __launch_bounds__(kThreads) void k_route(RouteParams p)
                 }
         uint64_t mine = 0;
         for (int j = 0; j < kt; ++j) {
-            const uint64_t best = wave_max_u64(pk[0]);
-            if (pk[0] == best) {
+            const uint32_t hh = (uint32_t)(pk[0] >> 32), hl = (uint32_t)pk[0];
+            const uint32_t mh = wave_max_u32(hh);
+            const uint64_t tied = __ballot(hh == mh);
+            uint32_t ml;
+            int win;
+            if (__builtin_popcountll(tied) == 1) {
+                win = __builtin_ctzll(tied);
+                ml = readlane_u32(hl, win);
+            } else {
+                ml = wave_max_u32(hh == mh ? hl : 0u);
+                win = __builtin_ctzll(__ballot(hh == mh && hl == ml));
+            }
+            if (l == win) {
 #pragma unroll
                 for (int i = 0; i + 1 < NTW; ++i) pk[i] = pk[i + 1];
                 pk[NTW - 1] = 0ull;
             }
-            if (l == j) mine = best;
+            if (l == j) mine = ((uint64_t)mh << 32) | ml;
         }
         if (kt == 0) continue;
         // (a round with no candidate left — k above the candidates, which
