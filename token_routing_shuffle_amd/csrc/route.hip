@@ -1,5 +1,9 @@
 // Route: gate GEMM on MFMA, synthetic affinity bias, top-k selection and
-// routing weights, fused in one kernel per 16-token tile.
+// routing weights.  Up to 64 experts (and in fp32) one kernel does it all
+// per 16-token tile; bf16 layers with more experts compute the gate in a
+// tiled GEMM kernel (64 x 128 or 128 x 256 / 128 x 128 output tiles, K
+// split into slices of partial logits) and the route kernel adds the slices
+// and selects, 8 tokens per block.
 //
 // The gate matrix rows are stored in slot order (the Sem-MoE placement is a
 // shuffle of the gate's columns: Japanese summary, technical overview
