@@ -140,6 +140,40 @@ def test_route_wide_gate(key):
               "max |dl| = %.3g" % (key, T, c.cfg.E, st["ties"], np.abs(l_gpu32 - l64).max()))
 
 
+# Routing-group shapes of the grouped sigmoid gate beyond 8 groups keeping 4
+# by their top-2 sums: the group scores are computed by lane segments whose
+# width depends on the number of groups (32 lanes for 2 groups, 16 for 3,
+# 8 for 5, 4 for 16, one lane for 64), over 1 to 8 summed keys.  Small H and
+# I keep the layers light; the last case has zero rows and no selection
+# bias, so group scores and keys tie exactly.
+RGROUPS = {
+    "g2_top8": (dict(n_rgroups=2, topk_rgroups=1, rgroup_topn=8), None),
+    "g3_e192": (dict(E=192, P=3, n_rgroups=3, topk_rgroups=2, rgroup_topn=3), None),
+    "g5_e320": (dict(E=320, P=5, n_rgroups=5, topk_rgroups=3, rgroup_topn=2), None),
+    "g16_top1": (dict(n_rgroups=16, topk_rgroups=5, rgroup_topn=1), None),
+    "g64_top4": (dict(n_rgroups=64, topk_rgroups=8, rgroup_topn=4), None),
+    "g16_ties": (dict(n_rgroups=16, topk_rgroups=3, rgroup_topn=3), "zero_rows_no_bias"),
+}
+
+
+@pytest.mark.parametrize("key", list(RGROUPS))
+def test_route_rgroup_shapes(key):
+    over, mut = RGROUPS[key]
+    mutate = {"zero_rows_no_bias": _zero_rows_no_bias}.get(mut)
+    c = hn.make_case("dsv3_decode", 160, profile_tokens=1024, mutate=mutate, H=512, I=256, I_shared=256,
+                     **over)
+    g = gpu_route(c)
+    l_gpu32 = hn.logits_orig(c, g["logits"].reshape(-1))
+    l64 = hn.oracle_logits(c)
+    assert (np.abs(l_gpu32 - l64) <= hn.logit_bound(c)).all()
+    st = hn.strict_route_parity(c, g["row_ptr"], g["slot"], g["w"], l_gpu32, "rgroups " + key)
+    if mut is not None:
+        assert st["ties"] > 0, "no token's selection depends on the tie-break"
+    hn.report("[route] rgroups %s: T=%d E=%d groups=%d keep=%d top-n=%d selection bit-exact on the GPU "
+              "logits (%d exact-tie tokens)" % (key, c.cfg.T, c.cfg.E, c.cfg.n_rgroups, c.cfg.topk_rgroups,
+                                                 c.cfg.rgroup_topn, st["ties"]))
+
+
 @pytest.mark.parametrize("key", list(CASES))
 def test_shuffle_bit_exact(key):
     c = case(key)
