@@ -587,14 +587,17 @@ __global__ __launch_bounds__(kThreads) void k_route(RouteParams p)
                 const float v = unordered_key((uint32_t)(gb >> 32));
                 sc = j == 0 ? v : sc + v;
             }
-            // topk_rgroups rounds of the wave maximum over (score, lower
-            // group id first), one candidate per group
-            uint64_t gk = (g < G && sub == 0) ? ((uint64_t)ordered_key(sc) << 32) | (0xFFFFFFFFu - (uint32_t)g) : 0ull;
+            // topk_rgroups rounds of the wave maximum over the groups' ordered
+            // scores, one candidate per group (its segment's first lane, so
+            // lane order is group order): of equal scores the lowest lane,
+            // the lower group id, wins; the winner drops out
+            uint32_t gh = (g < G && sub == 0) ? ordered_key(sc) : 0u;
             uint64_t kept = 0;
             for (int j = 0; j < p.topk_rgroups; ++j) {
-                const uint64_t b = wave_max_u64(gk);
-                if (gk == b) gk = 0ull;
-                kept |= 1ull << (0xFFFFFFFFu - (uint32_t)b);
+                const uint32_t mh = wave_max_u32(gh);
+                const int win = __builtin_ctzll(__ballot(gh == mh));
+                if (l == win) gh = 0u;
+                kept |= 1ull << (win / L);
             }
 #pragma unroll
             for (int i = 0; i < NTW; ++i) ok[i] = ok[i] && ((kept >> (oid[i] / gsize)) & 1ull);
