@@ -256,6 +256,8 @@ def test_route_workspace_gate_slices(m):
     from token_routing_shuffle_amd import workload as wl
     for name, T, over, S in [("dsv3_prefill", 8192, {}, 4),      # 64 wide tiles
                              ("dsv3_prefill", 4097, {}, 8),      # 33 wide tiles
+                             ("dsv3_prefill", 3969, {}, 8),      # 32 wide tiles: the smallest wide layer
+                             ("dsv3_prefill", 3968, {}, 4),      # 31: 62 x 2 narrow tiles
                              ("qwen3", 16384, {}, 2),            # 128 wide tiles of 128 experts
                              ("qwen3", 4100, dict(E=192, P=3), 4),  # 33 x 2, partial expert tile
                              ("prism", 8192, {}, 2),             # 64 x 2
